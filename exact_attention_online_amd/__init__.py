@@ -1,0 +1,182 @@
+"""Python binding of libattn.so: exact attention forward/backward and fp8 preparation on gfx950.
+
+Argument marshalling only.  Every step of the computation runs in the HIP kernels behind the C
+ABI declared in include/attn.h; torch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or a call fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "load", "library_path", "fwd", "bwd", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
+    "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+]
+
+F16, BF16, FP8_E4M3 = 0, 1, 2
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_fp8_prep", "attn_status_string")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libattn.so")
+
+
+def load():
+    """Load libattn.so (built in place by exact_attention_online_amd.build) and declare its ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise AttnError(f"{path} is missing: build it with `python -m exact_attention_online_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp] * 5 + [i] * 6 + [f, i] + [vp] * 3 + [vp]
+    lib.attn_fwd.restype = i
+    lib.attn_bwd_workspace_size.argtypes = [i] * 5
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 4 + [vp]
+    lib.attn_fp8_prep.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AttnError(f"libattn error {rc}: {load().attn_status_string(rc).decode()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise AttnError(f"unsupported dtype {t.dtype} (expected float16 or bfloat16)")
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise AttnError(f"expected q [B,Hq,N,d], k/v [B,Hkv,N,d]; got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise AttnError("q and k/v disagree in B, N or d")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise AttnError("tensors must be contiguous device tensors")
+        if t.device != q.device:
+            raise AttnError("tensors must be on one device")
+    return B, Hq, k.shape[1], N, d
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v) for fp16/bf16 q [B,Hq,N,d], k/v [B,Hkv,N,d] on one device."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise AttnError("q, k, v must share a dtype")
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+                           scale, dt, None, None, None, _stream(q.device)))
+    return out, lse
+
+
+def bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
+    return int(load().attn_bwd_workspace_size(B, Hq, Hkv, N, d))
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """dQ, dK, dV of L = <O, dO>; recomputes the probabilities from q, k, v and lse."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    dt = _dtype_code(q)
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise AttnError("o and do must match q in shape, dtype and layout")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise AttnError("lse must be float32 [B,Hq,N]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = bwd_workspace_size(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                           B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def fp8_prep(x, signs=None, out=None, descale=None):
+    """float32 x [B,H,N,d] -> (e4m3 codes as uint8 [B,H,N,d], float32 descale [B,H,ceil(N/128)])."""
+    torch = _torch()
+    if x.dim() != 4 or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise AttnError("x must be a contiguous float32 device tensor [B,H,N,d]")
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    sp = None
+    if signs is not None:
+        if signs.dtype != torch.int8 or signs.numel() != d or not signs.is_cuda:
+            raise AttnError("signs must be an int8 device tensor of length d")
+        sp = _ptr(signs)
+    _check(load().attn_fp8_prep(_ptr(x), _ptr(out), _ptr(descale), sp, B, H, N, d, _stream(x.device)))
+    return out, descale
+
+
+def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool = False, scale: float | None = None,
+            out=None, lse=None):
+    """Attention on e4m3 codes (uint8 [B,H,N,d]) with per-128-row float descales; O in bfloat16."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shapes(q8, k8, v8)
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8:
+            raise AttnError("fp8 operands are passed as uint8 e4m3 codes")
+    nb = (N + 127) // 128
+    for t, H in ((q_descale, Hq), (k_descale, Hkv), (v_descale, Hkv)):
+        if t.shape != (B, H, nb) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise AttnError("descales must be float32 [B,H,ceil(N/128)] device tensors")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    _check(load().attn_fwd(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+                           scale, FP8_E4M3, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _stream(q8.device)))
+    return out, lse

@@ -1,0 +1,112 @@
+// extern "C" entry points of libattn.so: argument checks on the host, then kernel dispatch.
+// Every check runs before any HIP call, so a rejected call enqueues nothing (and works on a
+// machine without a GPU).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "common.hpp"
+
+namespace eao {
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                      bool causal, float scale, bool bf16, void* workspace, hipStream_t stream);
+hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
+                           int d, hipStream_t stream);
+hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
+                          const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N, int d,
+                          bool causal, float scale, hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int Hq, int N, int d);
+}  // namespace eao
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+// Common shape checks; returns ATTN_OK or the status to report.
+int check_sizes(int B, int Hq, int Hkv, int N, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
+  // element counts must fit the kernels' 64-bit offsets and the 32-bit grid
+  const double elems = (double)B * Hq * N * d;
+  if (elems > 9.0e15) return ATTN_ERR_INVALID;
+  if ((double)B * Hq * ((N + 127) / 128) > 2.0e9) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size, scale or dtype)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128)";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+             int causal, float softmax_scale, int dtype, const float* q_descale, const float* k_descale,
+             const float* v_descale, attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_INVALID;
+  const int st = check_sizes(B, Hq, Hkv, N, d);
+  if (st != ATTN_OK) return st;
+  hipError_t e;
+  if (dtype == ATTN_FP8_E4M3) {
+    if (!aligned16(q_descale) || !aligned16(k_descale) || !aligned16(v_descale)) return ATTN_ERR_INVALID;
+    if (d != 128) return ATTN_ERR_UNSUPPORTED;
+    e = eao::launch_fwd_fp8((const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, q_descale,
+                            k_descale, v_descale, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
+                            (hipStream_t)stream);
+  } else {
+    if (q_descale || k_descale || v_descale) return ATTN_ERR_INVALID;
+    e = eao::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_scale, dtype == ATTN_BF16,
+                        (hipStream_t)stream);
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
+  if (check_sizes(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
+  return eao::bwd_workspace_bytes(B, Hq, N, d);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+             void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+             void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  const int st = check_sizes(B, Hq, Hkv, N, d);
+  if (st != ATTN_OK) return st;
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, N, d)) return ATTN_ERR_WORKSPACE;
+  const hipError_t e = eao::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal != 0,
+                                       softmax_scale, dtype == ATTN_BF16, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs, int B, int H, int N, int d,
+                  attn_stream_t stream) {
+  if (!aligned16(x) || !aligned16(x_fp8) || !aligned16(descale)) return ATTN_ERR_INVALID;
+  if (signs != nullptr && ((uintptr_t)signs & 15u) != 0) return ATTN_ERR_INVALID;
+  const int st = check_sizes(B, H, H, N, d);
+  if (st != ATTN_OK) return st;
+  const hipError_t e = eao::launch_fp8_prep(x, x_fp8, descale, signs, B, H, N, d, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Shared device helpers for the gfx950 attention kernels: MFMA wrappers, LDS swizzle and
+// transpose reads, cross-half lane exchange, 16-bit conversions.
+//
+// Lane layouts used throughout (checked on gfx950 with a layout probe):
+//   v_mfma_f32_32x32x16_{bf16,f16}:  lane l, g = l / 32
+//     A operand (8 x 16-bit): A[row = l % 32][k = 8g + e], e = 0..7
+//     B operand (8 x 16-bit): B[k = 8g + e][col = l % 32]
+//     C/D (16 x f32):         C[row = 8(r/4) + 4g + r%4][col = l % 32], r = 0..15
+//   Only the pairing of A slot (g, e) with B slot (g, e) matters for the sum over k, so any
+//   consistent relabelling of k is allowed; the kernels use that to feed a C tile straight
+//   back in as a B operand.
+//   ds_read_b64_tr_b16: in each group of 16 lanes, lane i reads 4 x 16-bit at its own address;
+//     lane j receives element (j % 4) of lanes (j / 4) + 4e, e = 0..3.  When lane i points at
+//     row (i / 4), columns 4(i % 4)..4(i % 4)+3 of a 4 x 16 block, lane j receives column j.
+//   v_permlane32_swap: exchanges lanes 0..31 of one operand with lanes 32..63 of the other;
+//     with both operands equal, {out0, out1} = {x[l % 32], x[l % 32 + 32]} on every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eao {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+typedef i16x4_t __attribute__((address_space(3))) lds_i16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// C += A * B on one 32x32x16 MFMA; BF16 selects bfloat16, otherwise fp16 operands.
+template <bool BF16>
+__device__ __forceinline__ f32x16_t mfma32x32x16(i16x8_t a, i16x8_t b, f32x16_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// Round-to-nearest-even conversion of two floats into a packed pair of 16-bit payloads.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (BF16) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+}
+
+// Eight consecutive accumulator entries -> one 8 x 16-bit MFMA operand.
+template <bool BF16>
+__device__ __forceinline__ i16x8_t pack8(const f32x16_t& x, int base) {
+  uint32_t w0 = pack2<BF16>(x[base + 0], x[base + 1]);
+  uint32_t w1 = pack2<BF16>(x[base + 2], x[base + 3]);
+  uint32_t w2 = pack2<BF16>(x[base + 4], x[base + 5]);
+  uint32_t w3 = pack2<BF16>(x[base + 6], x[base + 7]);
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+  u32x4_t w = {w0, w1, w2, w3};
+  return __builtin_bit_cast(i16x8_t, w);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_float(uint16_t x) {
+  if constexpr (BF16) {
+    return (float)__builtin_bit_cast(__bf16, x);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+}
+
+// max / sum of a value over lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS tile of rows of D 16-bit values (D/8 16-byte chunks per row).  Chunk c of row r lives at
+// chunk c ^ swz(r): for D = 128 the low two row bits move to the high two chunk bits, so 16
+// consecutive rows at one chunk, or 4 consecutive rows x 4 consecutive chunks, hit 16 distinct
+// chunk positions (the two read patterns of the kernels).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return row & 7;
+  }
+}
+
+// Index (in 16-byte chunks) of logical chunk c of row r.
+template <int D>
+__device__ __forceinline__ int chunk_index(int row, int c) {
+  return row * (D / 8) + (c ^ swz<D>(row));
+}
+
+// Index (in 16-bit elements) of element col of row r (col % 4 == 0 for transpose reads).
+template <int D>
+__device__ __forceinline__ int elem_index(int row, int col) {
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ i16x4_t ds_read_tr16(const short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+}  // namespace eao

@@ -1,0 +1,108 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
+ *
+ * Exact scaled-dot-product attention O = softmax(scale * Q K^T) V, computed by fused tiled
+ * kernels with an online softmax: the N x N score matrix never reaches HBM, each query row
+ * keeps a running maximum and running sum, the output is divided by the sum once at the end,
+ * and the per-row logsumexp is saved for the backward pass, which recomputes the scores and
+ * probabilities from Q, K, V and that logsumexp.
+ *   - "FlashAttention (NeurIPS 2022)" study notes, sections "Online Softmax", "FlashAttention"
+ *     and "Backward - Recomputation";
+ *   - "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning",
+ *     OpenReview discussion: unnormalised accumulator with one final division, logsumexp saved
+ *     instead of max and sum, causal key blocks after the query skipped, parallelism over
+ *     batch x head x query block, grouped-query attention (several query heads per K/V head);
+ *   - "FlashAttention-3: Fast and Accurate Attention with Asynchrony and Low-precision",
+ *     abstract: FP8 with block quantisation and incoherent processing.
+ *
+ * Conventions shared by every entry point
+ *   Pointers     device pointers (hipMalloc'd or equivalent), 16-byte aligned, owned by the
+ *                caller.  The library never allocates, frees or synchronises, holds no global
+ *                mutable state, and is safe to call from several host threads.
+ *   Layout       row-major contiguous [B, H, N, d]: Q, O, dO, dQ have H = Hq heads; K, V, dK,
+ *                dV have H = Hkv heads.  Query head h reads K/V head h / (Hq / Hkv).
+ *                LSE is float [B, Hq, N], natural logarithm.
+ *   Sizes        B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}; query and key lengths are
+ *                both N.  causal != 0 lets query i see keys j <= i only.
+ *   Scale        softmax_scale must be finite and > 0 (the usual value is 1 / sqrt(d)).
+ *   Streams      stream is a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *                work on that stream and returns; outputs are valid after the stream reaches
+ *                that point.  Outputs are overwritten, never accumulated into.
+ *   Errors       arguments are checked on the host before anything is enqueued; a failed check
+ *                returns a nonzero attn_status_t and enqueues nothing.  A launch failure
+ *                reported by the HIP runtime returns ATTN_ERR_HIP.  Faults inside a kernel show
+ *                up at the caller's next synchronisation.  NaN/Inf inputs propagate.
+ */
+#ifndef EXACT_ATTENTION_ONLINE_ATTN_H
+#define EXACT_ATTENTION_ONLINE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* attn_stream_t; /* a hipStream_t */
+
+typedef enum {
+  ATTN_F16 = 0,      /* IEEE binary16 storage */
+  ATTN_BF16 = 1,     /* bfloat16 storage */
+  ATTN_FP8_E4M3 = 2  /* OCP FP8 E4M3 (e4m3fn) storage with per-block float scales */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null/misaligned pointer, bad size, bad scale, bad dtype */
+  ATTN_ERR_UNSUPPORTED = 2, /* well-formed but not built: head dim other than 64/128, ... */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than attn_bwd_workspace_size() */
+  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+/* Forward pass.
+ *   q [B,Hq,N,d], k, v [B,Hkv,N,d] in `dtype`; o [B,Hq,N,d] in `dtype` (bfloat16 when dtype is
+ *   ATTN_FP8_E4M3); lse [B,Hq,N] float, natural log: lse = m + ln(sum_j exp(s_j - m)).
+ *   ATTN_FP8_E4M3 only: q_descale, k_descale, v_descale are float [B,H,ceil(N/128)] (H = Hq for
+ *   q, Hkv for k and v): the value of a stored code x in rows 128*i .. 128*i+127 of a head is
+ *   e4m3(x) * descale[i].  They must be NULL for ATTN_F16 / ATTN_BF16.
+ * Returns an attn_status_t. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+             const float* q_descale, const float* k_descale, const float* v_descale,
+             attn_stream_t stream);
+
+/* Bytes of device workspace attn_bwd needs: D = rowsum(dO * O) as float [B,Hq,N] plus a float
+ * dQ accumulator [B,Hq,N,d] (linear in N; no N x N buffer).  0 if the sizes are invalid. */
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
+
+/* Backward pass of L = <O, dO> ("FlashAttention (NeurIPS 2022)" notes, "Backward -
+ * Recomputation"; dV = P^T dO from the FlashAttention-2 discussion).
+ *   q, k, v, o, dout, lse as produced by/for attn_fwd with the same sizes, causal flag and
+ *   scale; dtype ATTN_F16 or ATTN_BF16.  Outputs dq [B,Hq,N,d] and dk, dv [B,Hkv,N,d] in
+ *   `dtype`; dk and dv are summed over the query heads that share each K/V head.
+ *   workspace: device memory of at least attn_bwd_workspace_size() bytes, 256-byte aligned,
+ *   owned by the caller; its contents on entry do not matter and are clobbered.
+ * Returns an attn_status_t. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+             void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* FP8 preparation ("FlashAttention-3 ...", abstract: block quantisation and incoherent
+ * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is
+ * first replaced by (row * signs) H_d / sqrt(d), H_d the Sylvester Hadamard matrix, computed in
+ * float32 with the butterfly stages in order h = 1, 2, ..., d/2.  Then for every block of 128
+ * rows of a head: scale = amax / 448 (1 if amax == 0), codes = e4m3(x / scale) rounded to
+ * nearest even and saturated to +-448.  Writes x_fp8 uint8 [B,H,N,d] and descale float
+ * [B,H,ceil(N/128)] (= scale).  Returns an attn_status_t. */
+int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs,
+                  int B, int H, int N, int d, attn_stream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ONLINE_ATTN_H */

@@ -1,0 +1,90 @@
+"""The C-ABI library loads without a GPU, exports what include/attn.h declares, and rejects bad
+arguments on the host before enqueuing anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_online_amd as eao
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# fake, 256-byte aligned device addresses: every call below fails validation before using them
+P = ctypes.c_void_p(0x7F0000001000)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = eao.load()
+    names = declared_functions()
+    assert set(names) == set(eao.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = eao.load()
+    for code in range(5):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, N=64, d=128, causal=0, scale=0.1, dtype=1,
+             qd=NULL, kd=NULL, vd=NULL)
+    a.update(kw)
+    return eao.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                               a["causal"], a["scale"], a["dtype"], a["qd"], a["kd"], a["vd"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(o=ctypes.c_void_p(0x7F0000001002)), 1), (dict(N=0), 1), (dict(B=0), 1),
+    (dict(Hq=3, Hkv=2), 1), (dict(Hkv=0), 1), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=-1.0), 1), (dict(dtype=7), 1), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(qd=P), 1), (dict(dtype=2), 1), (dict(dtype=2, qd=P, kd=P, vd=P, d=64), 2),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+def bwd(**kw):
+    a = dict(B=1, Hq=2, Hkv=1, N=64, d=128, causal=1, scale=0.1, dtype=1, ws=P, wsb=1 << 40)
+    a.update(kw)
+    ptrs = [a.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    return eao.load().attn_bwd(*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                               a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=NULL), 1), (dict(lse=ctypes.c_void_p(0x7F0000001004)), 1), (dict(Hq=5, Hkv=2), 1), (dict(N=-3), 1),
+    (dict(scale=0.0), 1), (dict(dtype=3), 1), (dict(dtype=2), 2), (dict(d=32), 2), (dict(ws=NULL), 3),
+    (dict(ws=ctypes.c_void_p(0x7F0000001010)), 3), (dict(wsb=100), 3),
+])
+def test_bwd_rejects_bad_arguments(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_prep_rejects_bad_arguments():
+    lib = eao.load()
+    assert lib.attn_fp8_prep(NULL, P, P, NULL, 1, 1, 128, 128, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, ctypes.c_void_p(0x7F0000001001), 1, 1, 128, 128, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 0, 128, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 128, 48, NULL) == 2
+
+
+def test_workspace_is_linear_in_n():
+    ws = eao.bwd_workspace_size
+    sizes = [ws(2, 8, 2, n, 128) for n in (1024, 2048, 4096, 8192)]
+    # D (4 bytes) + fp32 dQ accumulator (4 d bytes) per query row, rounded up to 256 bytes
+    for n, s in zip((1024, 2048, 4096, 8192), sizes):
+        rows = 2 * 8 * n
+        assert rows * (4 + 4 * 128) <= s <= rows * (4 + 4 * 128) + 256
+    assert ws(2, 8, 3, 1024, 128) == 0 and ws(1, 1, 1, 1, 80) == 0

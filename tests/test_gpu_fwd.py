@@ -1,0 +1,142 @@
+"""GPU parity of the forward kernels against the fp64 oracle (through the C ABI).
+
+Tolerances: O max-abs error <= 2e-3 (fp16) / 1.5e-2 (bf16) on unit-normal inputs; LSE max-abs
+<= 1e-3 (the statistics are fp32).  Small problems are compared element by element over every
+output; the large workloads on sampled query rows that the oracle computes row by row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_online_amd as eao
+from attn_inputs import WORKLOADS, draw, round_to
+from gpu_util import device, f64, sample_rows, to_dev
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"fp16": 2e-3, "bf16": 1.5e-2}
+TOL_LSE = 1e-3
+
+
+def _inputs(B, Hq, Hkv, N, d, dtype, seed):
+    _, q, k, v, _ = draw(B, Hq, Hkv, N, d, seed)
+    return round_to(q, dtype), round_to(k, dtype), round_to(v, dtype)
+
+
+def _run(q, k, v, causal, scale=None):
+    dev = device()
+    o, lse = eao.fwd(to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 127, 129, 200, 515])
+def test_forward_small_full(dtype, d, causal, N):
+    B, Hq, Hkv = 2, 3, 3
+    q, k, v = _inputs(B, Hq, Hkv, N, d, dtype, seed=N * 7 + d + causal)
+    o, lse = _run(q, k, v, causal)
+    ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(d))
+    assert np.abs(f64(o) - ro).max() <= TOL_O[dtype]
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (4, 2), (8, 8), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_gqa_full(Hq, Hkv, causal):
+    q, k, v = _inputs(2, Hq, Hkv, 300, 128, "bf16", seed=Hq * 10 + Hkv)
+    o, lse = _run(q, k, v, causal)
+    ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(128))
+    assert np.abs(f64(o) - ro).max() <= TOL_O["bf16"]
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+
+
+def test_small_fp16_workload_full():
+    w = WORKLOADS["small_fp16"]
+    q, k, v = _inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed=1)
+    o, lse = _run(q, k, v, w.causal)
+    ro, rlse = A.forward(q, k, v, w.causal, w.scale)
+    assert np.abs(f64(o) - ro).max() <= TOL_O["fp16"]
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+
+
+def _sampled_check(w, seed, heads, causal):
+    q, k, v = _inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed=seed)
+    o, lse = _run(q, k, v, causal)
+    o64, lse64 = f64(o), f64(lse)
+    rows = sample_rows(w.N, seed=seed)
+    for b, h in heads:
+        ro, rlse = A.forward_rows(q, k, v, causal, w.scale, b, h, rows)
+        assert np.abs(o64[b, h, rows] - ro).max() <= TOL_O[w.dtype], (b, h)
+        assert np.abs(lse64[b, h, rows] - rlse).max() <= TOL_LSE, (b, h)
+    assert np.isfinite(o64).all() and np.isfinite(lse64).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ablation_workload_sampled(causal):
+    w = WORKLOADS["ablation_bf16"]
+    _sampled_check(w, 2, [(0, 0), (3, 7), (7, 15)], causal)
+
+
+def test_long_workload_sampled():
+    w = WORKLOADS["long_bf16"]
+    _sampled_check(w, 3, [(0, 0), (0, 9), (0, 15)], True)
+
+
+def test_gqa_workload_sampled():
+    w = WORKLOADS["gqa_bf16"]
+    _sampled_check(w, 4, [(0, 0), (1, 5), (3, 31)], True)
+
+
+# ---------------------------------------------------------------- invariants on the device
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_key_returns_v_exactly(causal):
+    q, k, v = _inputs(2, 4, 2, 1, 128, "bf16", seed=5)
+    o, lse = _run(q, k, v, causal)
+    assert torch.equal(o.cpu(), v.repeat_interleave(2, dim=1))
+
+
+def test_causal_row0_is_v0_exactly():
+    q, k, v = _inputs(1, 2, 2, 333, 128, "bf16", seed=6)
+    o, _ = _run(q, k, v, True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+def test_causal_future_keys_do_not_matter_bitwise():
+    q, k, v = _inputs(1, 2, 2, 400, 128, "bf16", seed=7)
+    o1, l1 = _run(q, k, v, True)
+    i = 150
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i + 1:] = -k2[:, :, i + 1:] * 3
+    v2[:, :, i + 1:] = v2[:, :, i + 1:] * 5
+    o2, l2 = _run(q, k2, v2, True)
+    assert torch.equal(o1[:, :, : i + 1], o2[:, :, : i + 1])
+    assert torch.equal(l1[:, :, : i + 1], l2[:, :, : i + 1])
+
+
+def test_uniform_scores_average_v():
+    N = 300
+    _, k, v = _inputs(1, 1, 1, N, 128, "bf16", seed=8)
+    q = torch.zeros_like(k)
+    o, lse = _run(q, k, v, False)
+    want = f64(v).mean(axis=2, keepdims=True)
+    assert np.abs(f64(o) - want).max() <= 2e-3
+    assert np.abs(f64(lse) - np.log(N)).max() <= 1e-4
+
+
+def test_forward_is_deterministic():
+    q, k, v = _inputs(2, 4, 4, 700, 128, "bf16", seed=9)
+    o1, l1 = _run(q, k, v, True)
+    o2, l2 = _run(q, k, v, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_custom_scale():
+    q, k, v = _inputs(1, 2, 2, 130, 64, "fp16", seed=10)
+    o, lse = _run(q, k, v, False, scale=0.05)
+    ro, rlse = A.forward(q, k, v, False, 0.05)
+    assert np.abs(f64(o) - ro).max() <= TOL_O["fp16"]
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
