@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark: exact attention fwd+bwd on one MI355X, B=1, H=16, N=16384, d=128, bf16, causal.
+
+One step = one forward (attn_fwd) and one backward (attn_bwd's three phases) over the same
+seeded synthetic inputs, already resident in HBM.  FLOP convention: forward 4*B*H*N^2*d, halved
+for causal; backward 2.5x forward (five N^2*d contractions including the recomputation of S);
+fwd+bwd TFLOP/s = 3.5 * F_fwd / (time of a step).
+
+Prints one JSON line.  Besides the headline value it carries:
+  * roofline: the dominant kernel (the backward main kernel), its algorithmic FLOPs per launch
+    divided by its average launch time measured here with stream events, against the MI355X
+    dense bf16 MFMA peak; `traffic` is the HBM bytes per launch from the committed rocprofv3
+    counter summary, reported only while the kernel source still matches the one profiled;
+  * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "attention fwd / fwd+bwd TFLOPs/s (bf16, N=16k, d=128) + % of MFMA peak"
+WORKLOAD = "long_bf16"
+SEED = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_long_bf16_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_online_amd", "csrc", f) for f in ("bwd.hip", "common.hpp")]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip().lstrip("-* ").strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, do, target_s):
+    """The fp64 oracle (as it stands) on whole heads of the workload until target_s has passed."""
+    import numpy as np
+    from oracle import attention as A
+
+    try:
+        import threadpoolctl
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    f_head = 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
+    G = w.Hq // w.Hkv
+    t0 = time.perf_counter()
+    heads = 0
+    for h in range(w.Hq):
+        A.forward(q[:, h:h + 1], k[:, h // G:h // G + 1], v[:, h // G:h // G + 1], w.causal, w.scale, row_block=1024)
+        A.backward(q[:, h:h + 1], k[:, h // G:h // G + 1], v[:, h // G:h // G + 1], do[:, h:h + 1], w.causal, w.scale,
+                   row_block=1024)
+        heads += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(3.5 * f_head * heads / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"fp64 forward + backward of {heads} of {w.Hq} query heads (b=0) of the same "
+                  f"workload, {el:.1f} s; rate counted with the GPU's FLOP convention",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import WORKLOADS, draw, round_to
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    w = WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda:0")
+    _, q32, k32, v32, do32 = draw(w.B, w.Hq, w.Hkv, w.N, w.d, SEED, with_grad=True)
+    qc, kc, vc, doc = (round_to(x, w.dtype) for x in (q32, k32, v32, do32))
+    del q32, k32, v32, do32
+    q, k, v, do = (t.to(dev).contiguous() for t in (qc, kc, vc, doc))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(eao.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        eao.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        hook = (lambda i: ev[1 + i].record() if i in (1, 2) else None) if ev is not None else None
+        eao.bwd_phases(q, k, v, o, do, lse, w.causal, w.scale, ws, dq, dk, dv, between=hook)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_main_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[4]) for e in evs) / args.steps
+    for t in (o, lse, dq, dk, dv):
+        if not torch.isfinite(t).all():
+            print("non-finite output", file=sys.stderr)
+            sys.exit(1)
+
+    f_fwd = 4.0 * w.B * w.Hq * w.N * w.N * w.d / (2 if w.causal else 1)
+    ms_step = total_ms / args.steps
+    value = 3.5 * f_fwd / (ms_step * 1e-3) / 1e12
+    bwd_main_tflops = 2.5 * f_fwd / (bwd_main_ms * 1e-3) / 1e12
+    traffic = committed_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal fwd+bwd",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": w.causal,
+                   "seed": SEED, "pass": "fwd+bwd"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(2.5 * f_fwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "kernel_ms": {"attn_fwd": round(fwd_ms, 4), "bwd_main": round(bwd_main_ms, 4),
+                      "bwd_total": round(bwd_ms, 4)},
+        "roofline": {
+            "kernel": "bwd_main_kernel<bf16, d=128, causal>",
+            "bound": "mfma",
+            "achieved": round(bwd_main_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_main_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, doc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

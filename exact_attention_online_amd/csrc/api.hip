@@ -4,15 +4,21 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/attn.h"
 #include "common.hpp"
 
 namespace eao {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
-                      bool causal, float scale, bool bf16, void* workspace, hipStream_t stream);
+hipError_t launch_bwd_pre(const void* o, const void* dout, int B, int Hq, int N, int d, bool bf16, void* workspace,
+                          hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
+                           void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                           void* workspace, hipStream_t stream);
+hipError_t launch_bwd_convert(void* dq, int B, int Hq, int N, int d, float scale, bool bf16, void* workspace,
+                              hipStream_t stream);
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
                            int d, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
@@ -82,21 +88,62 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   return eao::bwd_workspace_bytes(B, Hq, N, d);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-             void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
-             void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return ATTN_ERR_INVALID;
-  if (!scale_ok(softmax_scale)) return ATTN_ERR_INVALID;
+// Shared checks of the backward entry points (pointer list, sizes, scale, dtype, workspace).
+static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int Hkv, int N, int d, float scale,
+                     int dtype, const void* workspace, size_t workspace_bytes) {
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
   const int st = check_sizes(B, Hq, Hkv, N, d);
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
   if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, N, d)) return ATTN_ERR_WORKSPACE;
-  const hipError_t e = eao::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal != 0,
-                                       softmax_scale, dtype == ATTN_BF16, workspace, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int d, int dtype,
+                        void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({o, dout}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return eao::launch_bwd_pre(o, dout, B, Hq, N, d, dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, void* workspace,
+                  size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, dout, lse, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return eao::launch_bwd_main(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
+                              dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int d, float softmax_scale, int dtype, void* workspace,
+                        size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({dq}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return eao::launch_bwd_convert(dq, B, Hq, N, d, softmax_scale, dtype == ATTN_BF16, workspace,
+                                 (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+             void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+             void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != ATTN_OK) return st;
+  const bool bf16 = dtype == ATTN_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  if (eao::launch_bwd_pre(o, dout, B, Hq, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (eao::launch_bwd_main(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
+                           s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (eao::launch_bwd_convert(dq, B, Hq, N, d, softmax_scale, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs, int B, int H, int N, int d,

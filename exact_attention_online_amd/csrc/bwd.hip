@@ -350,38 +350,59 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   }
 }
 
-template <bool BF16, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                               const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                               float scale, void* workspace, hipStream_t stream) {
-  const size_t rows = (size_t)B * Hq * N;
-  float* Dsum = (float*)workspace;
-  float* acc = (float*)((char*)workspace + ((rows * 4 + 255) / 256) * 256);
+static float* workspace_acc(void* workspace, size_t rows) {
+  return (float*)((char*)workspace + ((rows * 4 + 255) / 256) * 256);
+}
+
+template <bool BF16, int D>
+static hipError_t launch_bwd_pre_t(const void* o, const void* dout, size_t rows, void* workspace,
+                                   hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     (const uint16_t*)o, (const uint16_t*)dout, Dsum, acc, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkb = (N + kBwdKeys - 1) / kBwdKeys;
-  auto kern = bwd_main_kernel<BF16, D, CAUSAL>;
-  const size_t lds = BwdSmem<D>::BYTES;
-  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nkb * B * Hkv), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)dout, lse, Dsum, acc, (uint16_t*)dk, (uint16_t*)dv, Hq,
-                     Hkv, N, nkb, scale * kLog2e, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t n4 = rows * D / 4;
-  hipLaunchKernelGGL((bwd_dq_convert_kernel<BF16>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, acc,
-                     (uint16_t*)dq, n4, scale);
+                     (const uint16_t*)o, (const uint16_t*)dout, (float*)workspace, workspace_acc(workspace, rows),
+                     rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale,
-                      bool bf16, void* workspace, hipStream_t stream) {
+template <bool BF16, int D, bool CAUSAL>
+static hipError_t launch_bwd_main_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                    void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, void* workspace,
+                                    hipStream_t stream) {
+  const size_t rows = (size_t)B * Hq * N;
+  const int nkb = (N + kBwdKeys - 1) / kBwdKeys;
+  auto kern = bwd_main_kernel<BF16, D, CAUSAL>;
+  const size_t lds = BwdSmem<D>::BYTES;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(nkb * B * Hkv), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
+                     (const uint16_t*)v, (const uint16_t*)dout, lse, (const float*)workspace,
+                     workspace_acc(workspace, rows), (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, nkb,
+                     scale * kLog2e, scale);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_bwd_convert_t(void* dq, size_t rows, int d, float scale, void* workspace,
+                                       hipStream_t stream) {
+  const size_t n4 = rows * d / 4;
+  hipLaunchKernelGGL((bwd_dq_convert_kernel<BF16>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)workspace_acc(workspace, rows), (uint16_t*)dq, n4, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const void* o, const void* dout, int B, int Hq, int N, int d, bool bf16, void* workspace,
+                          hipStream_t stream) {
+  const size_t rows = (size_t)B * Hq * N;
+  if (bf16) return d == 128 ? launch_bwd_pre_t<true, 128>(o, dout, rows, workspace, stream)
+                            : launch_bwd_pre_t<true, 64>(o, dout, rows, workspace, stream);
+  return d == 128 ? launch_bwd_pre_t<false, 128>(o, dout, rows, workspace, stream)
+                  : launch_bwd_pre_t<false, 64>(o, dout, rows, workspace, stream);
+}
+
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
+                           void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                           void* workspace, hipStream_t stream) {
 #define EAO_BWD(BF, DD, CA) \
-  return launch_bwd_t<BF, DD, CA>(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, scale, workspace, stream)
+  return launch_bwd_main_t<BF, DD, CA>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, scale, workspace, stream)
   if (bf16) {
     if (d == 128) { if (causal) EAO_BWD(true, 128, true); else EAO_BWD(true, 128, false); }
     else { if (causal) EAO_BWD(true, 64, true); else EAO_BWD(true, 64, false); }
@@ -390,6 +411,13 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     else { if (causal) EAO_BWD(false, 64, true); else EAO_BWD(false, 64, false); }
   }
 #undef EAO_BWD
+}
+
+hipError_t launch_bwd_convert(void* dq, int B, int Hq, int N, int d, float scale, bool bf16, void* workspace,
+                              hipStream_t stream) {
+  const size_t rows = (size_t)B * Hq * N;
+  return bf16 ? launch_bwd_convert_t<true>(dq, rows, d, scale, workspace, stream)
+              : launch_bwd_convert_t<false>(dq, rows, d, scale, workspace, stream);
 }
 
 }  // namespace eao

@@ -88,6 +88,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
              void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* The three phases attn_bwd runs, for callers that schedule or time them separately.  Called
+ * in this order on one stream with the same arguments and workspace they produce exactly what
+ * attn_bwd produces (attn_bwd is these three calls).
+ *   attn_bwd_preprocess: D = rowsum(dO * O) into the workspace, dQ accumulator zeroed.
+ *   attn_bwd_main:       dK, dV written; dQ contributions added into the workspace accumulator
+ *                        (the probabilities are recomputed from q, k and lse).
+ *   attn_bwd_dq_convert: dq = softmax_scale * accumulator, rounded to `dtype`.
+ * Arguments mean what they mean for attn_bwd; each returns an attn_status_t. */
+int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int d, int dtype,
+                        void* workspace, size_t workspace_bytes, attn_stream_t stream);
+int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                  void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
+                  float softmax_scale, int dtype, void* workspace, size_t workspace_bytes,
+                  attn_stream_t stream);
+int attn_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int d, float softmax_scale, int dtype,
+                        void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
 /* FP8 preparation ("FlashAttention-3 ...", abstract: block quantisation and incoherent
  * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is
  * first replaced by (row * signs) H_d / sqrt(d), H_d the Sylvester Hadamard matrix, computed in
