@@ -40,6 +40,8 @@ int check_sizes(int B, int Hq, int Hkv, int N, int d) {
   if (elems > 9.0e15) return ATTN_ERR_INVALID;
   if ((double)B * Hq * ((N + 127) / 128) > 2.0e9) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // one head of one tensor is addressed with 32-bit byte offsets
+  if ((double)N * d * 4 > 2147483647.0) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

@@ -45,15 +45,18 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(i16x8_t a, i16x8_t b, f32x16_t 
   }
 }
 
-// Round-to-nearest-even conversion of two floats into a packed pair of 16-bit payloads.
+// Round-to-nearest-even conversion of two floats into a packed pair of 16-bit payloads
+// (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
   if constexpr (BF16) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   } else {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
   }
 }
 
@@ -111,6 +114,16 @@ __device__ __forceinline__ int chunk_index(int row, int c) {
 template <int D>
 __device__ __forceinline__ int elem_index(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 data-format word).  Loads at offsets
+// at or past `bytes` return zeros, which is how the kernels read ragged tails without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
 }
 
 __device__ __forceinline__ i16x4_t ds_read_tr16(const short* p) {

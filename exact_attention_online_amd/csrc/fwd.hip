@@ -20,19 +20,35 @@
 //     common.hpp).
 //   * Q stays in registers for the whole key loop (B operand of S^T).  K and V tiles of BC keys
 //     are loaded with 16-byte coalesced global loads into registers one tile ahead and stored
-//     into a double-buffered, XOR-swizzled LDS tile; K is read with ds_read_b128 and V through
+//     into double-buffered, row-padded LDS tiles; K is read with ds_read_b128 and V through
 //     ds_read_b64_tr_b16, which delivers V^T fragments without a separate transpose.
 //   * softmax in base 2: the running maximum is kept in units of s * scale * log2(e), so each
 //     probability is one fma plus one v_exp_f32.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace eao {
 
+// Headroom (log2 units) of the deferred rescaling: probabilities stay <= 2^kStaleMax.
+constexpr float kStaleMax = 8.0f;
+
+// LDS tiles use padded rows so that every address is a lane-dependent base plus a constant
+// (folded into the instruction's offset field):
+//   K tile: row stride D*2 + 16 bytes -- 16 consecutive rows read at one column (ds_read_b128)
+//           fall on 16 different 16-byte bank groups;
+//   V tile: row stride D*2 + 64 bytes -- 4 consecutive rows x 64 bytes (one 32-lane half of a
+//           ds_read_b64_tr_b16) fall on 4 different 64-byte bank groups.
 template <int D, int BC>
 struct FwdTile {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
   static constexpr int NLD = BC * CH / 256;        // chunks per thread per tile (K or V)
-  static constexpr int ELEMS = BC * D;             // 16-bit elements per tile
+  static constexpr int KSTR = D + 8;               // K row stride in 16-bit elements
+  static constexpr int VSTR = D + 32;              // V row stride in 16-bit elements
+  static constexpr int KELEMS = BC * KSTR;
+  static constexpr int VELEMS = BC * VSTR;
+  static constexpr int BUF = KELEMS + VELEMS;      // 16-bit elements per buffer (K then V)
+  static constexpr size_t BYTES = (size_t)2 * BUF * 2;
 };
 
 template <bool BF16, int D, int QB, int BC, bool CAUSAL>
@@ -43,9 +59,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   using T = FwdTile<D, BC>;
   constexpr int CH = T::CH, NLD = T::NLD, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int BR = 4 * QB * 32;
+  constexpr int KSTR = T::KSTR, VSTR = T::VSTR;
   extern __shared__ uint4 smem[];   // [2 buffers][K tile, V tile]
-  auto Ks = [&](int buf) { return smem + buf * 2 * BC * CH; };
-  auto Vs = [&](int buf) { return smem + buf * 2 * BC * CH + BC * CH; };
+  short* const sm = (short*)smem;
+  auto Ks = [&](int buf) { return sm + buf * T::BUF; };
+  auto Vs = [&](int buf) { return sm + buf * T::BUF + T::KELEMS; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -92,20 +110,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
+  // K/V of this head through bounds-checked buffer loads: keys >= N read as zeros
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kp, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vp, (uint32_t)N * D * 2);
   uint4 kreg[NLD], vreg[NLD];
   auto load_tile = [&](int kt0) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int cidx = tid + 256 * i;
       const int row = cidx / CH, ch = cidx % CH;
-      const int key = kt0 + row;
-      if (key < N) {
-        kreg[i] = *(const uint4*)(Kp + (size_t)key * D + ch * 8);
-        vreg[i] = *(const uint4*)(Vp + (size_t)key * D + ch * 8);
-      } else {
-        kreg[i] = uint4{0, 0, 0, 0};
-        vreg[i] = uint4{0, 0, 0, 0};
-      }
+      const uint32_t off = ((uint32_t)(kt0 + row) * D + ch * 8) * 2;
+      kreg[i] = buffer_load16(krs, off);
+      vreg[i] = buffer_load16(vrs, off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -113,24 +129,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     for (int i = 0; i < NLD; ++i) {
       const int cidx = tid + 256 * i;
       const int row = cidx / CH, ch = cidx % CH;
-      Ks(buf)[chunk_index<D>(row, ch)] = kreg[i];
-      Vs(buf)[chunk_index<D>(row, ch)] = vreg[i];
+      *(uint4*)(Ks(buf) + row * KSTR + ch * 8) = kreg[i];
+      *(uint4*)(Vs(buf) + row * VSTR + ch * 8) = vreg[i];
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
+  // One key tile: S^T, (masked) online softmax, O^T += V^T P^T.  MASK selects the variant with
+  // causal / key-tail masking; only tiles that cross the diagonal or the end of the keys need it.
+  auto tile = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int kt0 = j * BC;
     const bool has_next = j + 1 < ntiles;
     if (has_next) load_tile(kt0 + BC);
 
     const bool active = (qw < N) && (!CAUSAL || kt0 <= qw_last);
     if (active) {
-      const uint4* Kb = Ks(j & 1);
-      const short* Vb = (const short*)Vs(j & 1);
+      const short* Kb = Ks(j & 1);
+      const short* Vb = Vs(j & 1);
       // ---- S^T = K Q^T
       f32x16_t s[QB][KB];
 #pragma unroll
@@ -141,18 +156,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const i16x8_t a = __builtin_bit_cast(i16x8_t, Kb[chunk_index<D>(32 * kb + l32, 2 * kk + g)]);
+          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + (32 * kb + l32) * KSTR + 16 * kk + 8 * g));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16<BF16>(a, qf[qb][kk], s[qb][kb]);
         }
       }
-      // ---- mask, online softmax
-      const bool need_mask = (kt0 + BC > N) || (CAUSAL && kt0 + BC - 1 > qw);
+      // ---- online softmax
       i16x8_t pf[QB][KB][2];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw + 32 * qb + l32;
-        if (need_mask) {
+        if constexpr (MASK) {
+          const int qrow = qw + 32 * qb + l32;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -166,11 +180,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = max_halves(mx);
-        const float mnew = fmaxf(m[qb], mx * c);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);
-        m[qb] = mnew;
+        const float mt = max_halves(mx) * c;
+        // The accumulator is rescaled only when some row's maximum has grown by more than
+        // kStaleMax (log2 units) since the last rescale; otherwise the stale maximum is kept,
+        // probabilities stay <= 2^kStaleMax, and the final division by l (computed against the
+        // same maximum) gives the same result.
+        // The decision is per row (alpha is exactly 1 where the row keeps its maximum), so a
+        // row's result never depends on other rows; the branch only skips the multiplies when
+        // no row of the wave needs them.
+        const bool grow = mt > m[qb] + kStaleMax;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - mt) : 1.f;
+          // an opaque (volatile) definition of alpha pins the multiplies below inside this
+          // branch; left alone, the compiler hoists them and runs them on every tile
+          asm volatile("" : "+v"(alpha));
+          m[qb] = grow ? mt : m[qb];
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+        }
+        const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -180,9 +209,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
             s[qb][kb][r] = p;
             rs += p;
           }
-        l[qb] = l[qb] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+        l[qb] += rs;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           pf[qb][kb][0] = pack8<BF16>(s[qb][kb], 0);
@@ -199,8 +226,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int col = 32 * db + 16 * (G16 & 1) + 4 * (li & 3);
-            const i16x4_t lo = ds_read_tr16(Vb + elem_index<D>(krow, col));
-            const i16x4_t hi = ds_read_tr16(Vb + elem_index<D>(krow + 8, col));
+            const i16x4_t lo = ds_read_tr16(Vb + krow * VSTR + col);
+            const i16x4_t hi = ds_read_tr16(Vb + (krow + 8) * VSTR + col);
             const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32x32x16<BF16>(a, pf[qb][kb][t], o[qb][db]);
@@ -210,7 +237,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 
     if (has_next) store_tile((j + 1) & 1);
     __syncthreads();
-  }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  // tiles [0, jmask) need no masking for any wave of the workgroup
+  const int jmask = min(ntiles, CAUSAL ? min(q0, N) / BC : N / BC);
+  int j = 0;
+  for (; j < jmask; ++j) tile(j, std::false_type{});
+  for (; j < ntiles; ++j) tile(j, std::true_type{});
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
 #pragma unroll
@@ -241,7 +278,7 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
   constexpr int BR = 4 * QB * 32;
   const int nqb = (N + BR - 1) / BR;
   const int BH = B * Hq;
-  const size_t lds = (size_t)4 * BC * D * 2;
+  const size_t lds = FwdTile<D, BC>::BYTES;
   auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
