@@ -7,7 +7,7 @@ for causal; backward 2.5x forward (five N^2*d contractions including the recompu
 fwd+bwd TFLOP/s = 3.5 * F_fwd / (time of a step).
 
 Prints one JSON line.  Besides the headline value it carries:
-  * roofline: the dominant kernel (the backward main kernel), its algorithmic FLOPs per launch
+  * roofline: the dominant kernel (the backward dK/dV kernel), its algorithmic FLOPs per launch
     divided by its average launch time measured here with stream events, against the MI355X
     dense bf16 MFMA peak; `traffic` is the HBM bytes per launch from the committed rocprofv3
     counter summary, reported only while the kernel source still matches the one profiled;
@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 
 METRIC = "attention fwd / fwd+bwd TFLOPs/s (bf16, N=16k, d=128) + % of MFMA peak"
 WORKLOAD = "long_bf16"
 SEED = 3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_long_bf16_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_long_bf16_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_online_amd", "csrc", f) for f in ("bwd.hip", "common.hpp")]
 
 
@@ -136,10 +136,8 @@ def main():
         eao.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        hook = (lambda i: ev[1 + i].record() if i in (1, 2) else None) if ev is not None else None
+        hook = (lambda i: ev[1 + i].record() if i in (1, 2, 3) else None) if ev is not None else None
         eao.bwd_phases(q, k, v, o, do, lse, w.causal, w.scale, ws, dq, dk, dv, between=hook)
-        if ev is not None:
-            ev[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -154,7 +152,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_main_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    dkdv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    dq_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[4]) for e in evs) / args.steps
     for t in (o, lse, dq, dk, dv):
         if not torch.isfinite(t).all():
@@ -164,7 +163,10 @@ def main():
     f_fwd = 4.0 * w.B * w.Hq * w.N * w.N * w.d / (2 if w.causal else 1)
     ms_step = total_ms / args.steps
     value = 3.5 * f_fwd / (ms_step * 1e-3) / 1e12
-    bwd_main_tflops = 2.5 * f_fwd / (bwd_main_ms * 1e-3) / 1e12
+    # the dK/dV kernel does four of the backward's contractions (S, dP, dV, dK): 2.0 x F_fwd;
+    # the dQ kernel three (S, dP, dQ: 1.5 x F_fwd), two of them recomputations
+    dkdv_tflops = 2.0 * f_fwd / (dkdv_ms * 1e-3) / 1e12
+    dq_tflops = 1.5 * f_fwd / (dq_ms * 1e-3) / 1e12
     traffic = committed_traffic()
     out = {
         "metric": METRIC,
@@ -186,15 +188,17 @@ def main():
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(2.5 * f_fwd / (bwd_ms * 1e-3) / 1e12, 2),
-        "kernel_ms": {"attn_fwd": round(fwd_ms, 4), "bwd_main": round(bwd_main_ms, 4),
+        "kernel_ms": {"attn_fwd": round(fwd_ms, 4), "bwd_dkdv": round(dkdv_ms, 4), "bwd_dq": round(dq_ms, 4),
                       "bwd_total": round(bwd_ms, 4)},
+        "kernel_tflops": {"attn_fwd": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2), "bwd_dkdv": round(dkdv_tflops, 2),
+                          "bwd_dq": round(dq_tflops, 2)},
         "roofline": {
-            "kernel": "bwd_main_kernel<bf16, d=128, causal>",
+            "kernel": "bwd_dkdv_kernel<bf16, d=128, causal>",
             "bound": "mfma",
-            "achieved": round(bwd_main_tflops, 2),
+            "achieved": round(dkdv_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(bwd_main_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dkdv_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
     }

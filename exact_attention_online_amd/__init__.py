@@ -16,8 +16,8 @@ __all__ = [
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_main",
-           "attn_bwd_dq_convert", "attn_fp8_prep", "attn_status_string")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
+           "attn_bwd_dq", "attn_fp8_prep", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -49,10 +49,10 @@ def load():
     lib.attn_bwd.restype = i
     lib.attn_bwd_preprocess.argtypes = [vp] * 2 + [i] * 6 + [vp, sz, vp]
     lib.attn_bwd_preprocess.restype = i
-    lib.attn_bwd_main.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, sz, vp]
-    lib.attn_bwd_main.restype = i
-    lib.attn_bwd_dq_convert.argtypes = [vp] + [i] * 5 + [f, i, vp, sz, vp]
-    lib.attn_bwd_dq_convert.restype = i
+    lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd_dkdv.restype = i
+    lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd_dq.restype = i
     lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 4 + [vp]
     lib.attn_fp8_prep.restype = i
     lib.attn_status_string.argtypes = [i]
@@ -149,20 +149,22 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
 
 
 def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, between=None):
-    """attn_bwd as its three phases; ``between(i)`` (if given) is called before phase i = 0, 1, 2
-    and after the last one with i = 3, e.g. to record stream events around the main phase."""
+    """attn_bwd as its three phases (preprocess, dK/dV, dQ); ``between(i)`` (if given) is called
+    before phase i = 0, 1, 2 and after the last one with i = 3, e.g. to record stream events."""
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     dt = _dtype_code(q)
     lib, st = load(), _stream(q.device)
     wsb = workspace.numel() * workspace.element_size()
     hook = between or (lambda i: None)
+    causal, scale = int(bool(causal)), float(scale)
     hook(0)
     _check(lib.attn_bwd_preprocess(_ptr(o), _ptr(do), B, Hq, Hkv, N, d, dt, _ptr(workspace), wsb, st))
     hook(1)
-    _check(lib.attn_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
-                             int(bool(causal)), float(scale), dt, _ptr(workspace), wsb, st))
+    _check(lib.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
+                             causal, scale, dt, _ptr(workspace), wsb, st))
     hook(2)
-    _check(lib.attn_bwd_dq_convert(_ptr(dq), B, Hq, Hkv, N, d, float(scale), dt, _ptr(workspace), wsb, st))
+    _check(lib.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq), B, Hq, Hkv, N, d, causal,
+                           scale, dt, _ptr(workspace), wsb, st))
     hook(3)
     return dq, dk, dv
 

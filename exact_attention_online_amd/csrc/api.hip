@@ -14,11 +14,12 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_pre(const void* o, const void* dout, int B, int Hq, int N, int d, bool bf16, void* workspace,
                           hipStream_t stream);
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                           void* workspace, hipStream_t stream);
-hipError_t launch_bwd_convert(void* dq, int B, int Hq, int N, int d, float scale, bool bf16, void* workspace,
-                              hipStream_t stream);
+                           const void* workspace, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
+                         int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                         const void* workspace, hipStream_t stream);
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
                            int d, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
@@ -112,23 +113,25 @@ int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv,
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
-                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, void* workspace,
-                  size_t workspace_bytes, attn_stream_t stream) {
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+                  const void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   const int st = check_bwd({q, k, v, dout, lse, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
                            workspace_bytes);
   if (st != ATTN_OK) return st;
-  return eao::launch_bwd_main(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
+  return eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
                               dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int d, float softmax_scale, int dtype, void* workspace,
-                        size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({dq}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace, workspace_bytes);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq, int B,
+                int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, const void* workspace,
+                size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, dout, lse, dq}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
+                           workspace_bytes);
   if (st != ATTN_OK) return st;
-  return eao::launch_bwd_convert(dq, B, Hq, N, d, softmax_scale, dtype == ATTN_BF16, workspace,
-                                 (hipStream_t)stream) == hipSuccess
+  return eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
+                            dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -141,10 +144,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   const bool bf16 = dtype == ATTN_BF16;
   const hipStream_t s = (hipStream_t)stream;
   if (eao::launch_bwd_pre(o, dout, B, Hq, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
-  if (eao::launch_bwd_main(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
+  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
                            s) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (eao::launch_bwd_convert(dq, B, Hq, N, d, softmax_scale, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s) !=
+      hipSuccess)
+    return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 

@@ -71,8 +71,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const float* q_descale, const float* k_descale, const float* v_descale,
              attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: D = rowsum(dO * O) as float [B,Hq,N] plus a float
- * dQ accumulator [B,Hq,N,d] (linear in N; no N x N buffer).  0 if the sizes are invalid. */
+/* Bytes of device workspace attn_bwd needs: D = rowsum(dO * O) as float [B,Hq,N] (linear in N;
+ * no N x N buffer).  0 if the sizes are invalid. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /* Backward pass of L = <O, dO> ("FlashAttention (NeurIPS 2022)" notes, "Backward -
@@ -88,22 +88,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
              void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
-/* The three phases attn_bwd runs, for callers that schedule or time them separately.  Called
- * in this order on one stream with the same arguments and workspace they produce exactly what
- * attn_bwd produces (attn_bwd is these three calls).
- *   attn_bwd_preprocess: D = rowsum(dO * O) into the workspace, dQ accumulator zeroed.
- *   attn_bwd_main:       dK, dV written; dQ contributions added into the workspace accumulator
- *                        (the probabilities are recomputed from q, k and lse).
- *   attn_bwd_dq_convert: dq = softmax_scale * accumulator, rounded to `dtype`.
+/* The three phases attn_bwd runs, for callers that schedule or time them separately.  With the
+ * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
+ * streams once preprocess is complete) produces exactly what attn_bwd produces; attn_bwd is
+ * these three calls on one stream.
+ *   attn_bwd_preprocess: D = rowsum(dO * O) into the workspace.
+ *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
+ *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
  * Arguments mean what they mean for attn_bwd; each returns an attn_status_t. */
 int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int d, int dtype,
                         void* workspace, size_t workspace_bytes, attn_stream_t stream);
-int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
-                  float softmax_scale, int dtype, void* workspace, size_t workspace_bytes,
+                  float softmax_scale, int dtype, const void* workspace, size_t workspace_bytes,
                   attn_stream_t stream);
-int attn_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int d, float softmax_scale, int dtype,
-                        void* workspace, size_t workspace_bytes, attn_stream_t stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                int dtype, const void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* FP8 preparation ("FlashAttention-3 ...", abstract: block quantisation and incoherent
  * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is
