@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     kf[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(krs, off));
     vf[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(vrs, off));
   }
+  wait_all_loads();
   f32x16_t dvacc[DB], dkacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -213,6 +214,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         sacc = mfma32x32x16<BF16>(aq, kf[kk], sacc);
         dp = mfma32x32x16<BF16>(ado, vf[kk], dp);
       }
+      // scheduling hint: the LDS reads of the S/dP operands run two MFMA pairs ahead of their
+      // use (mask 0x100 = LDS reads, 0x008 = MFMA); left alone the compiler issues each read
+      // right before its MFMA and the single wave per SIMD waits out every LDS latency
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2, 0);
+#pragma unroll
+      for (int i = 0; i < KK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
       // P and dS; lane owns key kw + l32, register r holds query q0 + 32qs + 8(r/4) + 4g + r%4
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -249,6 +259,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           const i16x8_t aq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
           dkacc[db] = mfma32x32x16<BF16>(aq, sb[t], dkacc[db]);
         }
+      }
+      // scheduling hint: the transposed reads of dO^T / Q^T run two MFMA pairs ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * 2, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
       }
     }
     if (has_next) store_tile(buf ^ 1);
@@ -351,6 +368,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // rows past the end: LSE = +inf gives P = 0
   const float lse2 = qrow < N ? LSE[q_row0 + qrow] * kLog2e : INFINITY;
   const float dd = qrow < N ? Dsum[q_row0 + qrow] : 0.f;
+  wait_all_loads();
 
   f32x16_t acc[DB];
 #pragma unroll

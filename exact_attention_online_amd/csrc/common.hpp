@@ -126,6 +126,13 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
+// Wait for every outstanding memory operation.  Issued once after the loads of loop-invariant
+// operands: without it the counter-based waits the compiler places inside the loop (it cannot
+// tell that those loads finished in an earlier iteration) also wait for the loop's own
+// prefetches, because the counters drain in order, which exposes the full load latency on
+// every iteration.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ i16x4_t ds_read_tr16(const short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
       qf[kk] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  wait_all_loads();
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};

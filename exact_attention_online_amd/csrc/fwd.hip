@@ -97,6 +97,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   }
 
+  wait_all_loads();
+
   f32x16_t o[QB][DB];
   float m[QB], l[QB];
 #pragma unroll
