@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the warmup, run one plain device-to-device copy of MIB MiB (a kernel of "
+                         "known traffic that scales HBM byte counters read under a profiler)")
     return ap.parse_args()
 
 
@@ -138,6 +141,16 @@ def main():
             ev[1].record()
         hook = (lambda i: ev[1 + i].record() if i in (1, 2, 3) else None) if ev is not None else None
         eao.bwd_phases(q, k, v, o, do, lse, w.causal, w.scale, ws, dq, dk, dv, between=hook)
+
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {args.copy_calibration} MiB read + {args.copy_calibration} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         step()
