@@ -126,6 +126,14 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
+// Direct load into LDS: each lane fetches 16 bytes at byte offset `off` of the buffer, and lane l's
+// bytes land at dst + 16 l (dst must be the same on every lane of the wave).  Loads past the
+// buffer's end deliver zeros.  Completion is tracked by the vector-memory counter.  (A device-only
+// function: the host pass never sees the cast to the LDS address space.)
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, short* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)off, 0, 0, 0);
+}
+
 // Wait for every outstanding memory operation.  Issued once after the loads of loop-invariant
 // operands: without it the counter-based waits the compiler places inside the loop (it cannot
 // tell that those loads finished in an earlier iteration) also wait for the loop's own

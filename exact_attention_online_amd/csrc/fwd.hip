@@ -19,9 +19,13 @@
 //     to 16-bit, is directly the B operand (P^T) of the second MFMA (k relabelled, see
 //     common.hpp).
 //   * Q stays in registers for the whole key loop (B operand of S^T).  K and V tiles of BC keys
-//     are loaded with 16-byte coalesced global loads into registers one tile ahead and stored
-//     into double-buffered, row-padded LDS tiles; K is read with ds_read_b128 and V through
+//     go straight from HBM into double-buffered, XOR-swizzled LDS tiles with direct
+//     buffer -> LDS loads (no staging registers); K is read with ds_read_b128 and V through
 //     ds_read_b64_tr_b16, which delivers V^T fragments without a separate transpose.
+//   * software pipeline: K runs one tile ahead of V, so while the softmax of tile j runs on the
+//     vector ALU, the MFMAs of S^T for tile j + 1 are already issued; both sit in one basic block
+//     and the scheduler interleaves them (a single wave keeps the matrix core and the vector
+//     ALU busy together).
 //   * softmax in base 2: the running maximum is kept in units of s * scale * log2(e), so each
 //     probability is one fma plus one v_exp_f32.
 #include <type_traits>
@@ -33,23 +37,21 @@ namespace eao {
 // Headroom (log2 units) of the deferred rescaling: probabilities stay <= 2^kStaleMax.
 constexpr float kStaleMax = 8.0f;
 
-// LDS tiles use padded rows so that every address is a lane-dependent base plus a constant
-// (folded into the instruction's offset field):
-//   K tile: row stride D*2 + 16 bytes -- 16 consecutive rows read at one column (ds_read_b128)
-//           fall on 16 different 16-byte bank groups;
-//   V tile: row stride D*2 + 64 bytes -- 4 consecutive rows x 64 bytes (one 32-lane half of a
-//           ds_read_b64_tr_b16) fall on 4 different 64-byte bank groups.
+// LDS tiles (K and V, [BC keys][D], double-buffered each) are unpadded, with 16-byte chunks
+// XOR-swizzled by row (swz in common.hpp): a ds_read_b128 of 16 consecutive rows at one
+// chunk, and a ds_read_b64_tr_b16 of 4 consecutive rows x 4 consecutive chunks, both hit
+// distinct bank groups.  Unpadded rows let the tiles be filled by direct buffer -> LDS loads
+// (each instruction moves 64 lanes x 16 bytes to 1 KB of consecutive LDS; the swizzle is
+// applied by choosing which global chunk each lane fetches), so staging takes no registers.
 template <int D, int BC>
 struct FwdTile {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
-  static constexpr int NLD = BC * CH / 256;        // chunks per thread per tile (K or V)
-  static constexpr int KSTR = D + 8;               // K row stride in 16-bit elements
-  static constexpr int VSTR = D + 32;              // V row stride in 16-bit elements
-  static constexpr int KELEMS = BC * KSTR;
-  static constexpr int VELEMS = BC * VSTR;
-  static constexpr int BUF = KELEMS + VELEMS;      // 16-bit elements per buffer (K then V)
-  static constexpr size_t BYTES = (size_t)2 * BUF * 2;
+  static constexpr int ELEMS = BC * D;             // 16-bit elements per tile
+  static constexpr int PIECES = ELEMS * 2 / 1024;  // 1 KB direct-load pieces per tile
 };
+
+using Par0 = std::integral_constant<int, 0>;
+using Par1 = std::integral_constant<int, 1>;
 
 template <bool BF16, int D, int QB, int BC, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
@@ -57,16 +59,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int BH, int nqb,
     float c /* softmax_scale * log2(e) */) {
   using T = FwdTile<D, BC>;
-  constexpr int CH = T::CH, NLD = T::NLD, KK = D / 16, DB = D / 32, KB = BC / 32;
+  constexpr int CH = T::CH, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int BR = 4 * QB * 32;
-  constexpr int KSTR = T::KSTR, VSTR = T::VSTR;
-  extern __shared__ uint4 smem[];   // [2 buffers][K tile, V tile]
-  short* const sm = (short*)smem;
-  auto Ks = [&](int buf) { return sm + buf * T::BUF; };
-  auto Vs = [&](int buf) { return sm + buf * T::BUF + T::KELEMS; };
+  static_assert(T::PIECES % 4 == 0, "each wave moves the same number of pieces");
+  // four distinct LDS objects, so that the compiler can tell a direct load into one buffer from
+  // a read of another and does not wait for the load before the read
+  __shared__ __attribute__((aligned(1024))) short k_lds0[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) short k_lds1[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) short v_lds0[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) short v_lds1[T::ELEMS];
+  auto Ks = [&](auto par) -> short* {
+    if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
+  };
+  auto Vs = [&](auto par) -> short* {
+    if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int G16 = lane >> 4, li = lane & 15;
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
@@ -75,8 +86,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const size_t q_off = ((size_t)b * Hq + h) * (size_t)N * D;
   const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
   const uint16_t* Qp = Q + q_off;
-  const uint16_t* Kp = K + kv_off;
-  const uint16_t* Vp = V + kv_off;
 
   const int q0 = qblk * BR;
   const int qw = q0 + w * QB * 32;          // first query row of this wave
@@ -97,8 +106,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   }
 
-  wait_all_loads();
-
   f32x16_t o[QB][DB];
   float m[QB], l[QB];
 #pragma unroll
@@ -113,143 +120,193 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int ntiles = (kend + BC - 1) / BC;
 
   // K/V of this head through bounds-checked buffer loads: keys >= N read as zeros
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kp, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vp, (uint32_t)N * D * 2);
-  uint4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int kt0) {
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, (uint32_t)N * D * 2);
+  // direct loads: piece p = 4i + w of a tile; lane l fills LDS chunk 64p + l (row (64p + l) / CH,
+  // physical chunk l % CH) with the logical chunk that the swizzle puts there
+  uint32_t goff[T::PIECES / 4];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      const uint32_t off = ((uint32_t)(kt0 + row) * D + ch * 8) * 2;
-      kreg[i] = buffer_load16(krs, off);
-      vreg[i] = buffer_load16(vrs, off);
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int i = 0; i < T::PIECES / 4; ++i) {
+    const int p = 64 * (4 * i + w) + lane;
+    const int row = p / CH, pch = p % CH;
+    goff[i] = ((uint32_t)row * D + ((pch ^ swz<D>(row)) << 3)) * 2;
+  }
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, short* dst, int kt0) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      *(uint4*)(Ks(buf) + row * KSTR + ch * 8) = kreg[i];
-      *(uint4*)(Vs(buf) + row * VSTR + ch * 8) = vreg[i];
-    }
+    for (int i = 0; i < T::PIECES / 4; ++i)
+      buffer_load16_lds(rs, dst + 512 * (4 * i + w), goff[i] + (uint32_t)kt0 * D * 2);
   };
 
-  // One key tile: S^T, (masked) online softmax, O^T += V^T P^T.  MASK selects the variant with
-  // causal / key-tail masking; only tiles that cross the diagonal or the end of the keys need it.
-  auto tile = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int kt0 = j * BC;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(kt0 + BC);
+  // loop-invariant LDS offsets (16-bit units): K rows l32 (+32 kb) at chunk 2kk + g; V^T
+  // transposed reads at rows 4(G16/2) + li/4 (+8h, +16t, +32kb), columns 32db + 16(G16%2) + 4(li%4)
+  int off_k[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) off_k[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
+  int off_v[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      off_v[db][hh] = elem_index<D>(4 * (G16 >> 1) + (li >> 2) + 8 * hh, 32 * db + 16 * (G16 & 1) + 4 * (li & 3));
 
-    const bool active = (qw < N) && (!CAUSAL || kt0 <= qw_last);
-    if (active) {
-      const short* Kb = Ks(j & 1);
-      const short* Vb = Vs(j & 1);
-      // ---- S^T = K Q^T
-      f32x16_t s[QB][KB];
+  // a wave takes part in tiles [0, jact): under causal masking, tiles whose first key lies after
+  // the wave's last query row are skipped (the wave still helps stage them)
+  const int jact = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, qw_last / BC + 1) : ntiles);
+
+  // S^T = K Q^T for the key tile in K buffer `par`
+  auto compute_s = [&](auto par, f32x16_t (&s)[QB][KB]) {
+    const short* Kb = Ks(par);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16_t{};
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16_t{};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + (32 * kb + l32) * KSTR + 16 * kk + 8 * g));
+      for (int kb = 0; kb < KB; ++kb) {
+        const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + 32 * kb * D + off_k[kk]));
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16<BF16>(a, qf[qb][kk], s[qb][kb]);
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16<BF16>(a, qf[qb][kk], s[qb][kb]);
       }
-      // ---- online softmax
-      i16x8_t pf[QB][KB][2];
+    }
+  };
+
+  // staging of one iteration: K_{j+2} replaces K_j (read while computing S^T of tile j, one
+  // iteration ago), V_{j+1} replaces V_{j-1} (read one iteration ago)
+  // (tile j lives in K and V buffers j % 2 = par)
+  auto stage = [&](int j, auto par) {
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    if (j + 2 < ntiles) load_tile(krs, Ks(par), (j + 2) * BC);
+    if (j + 1 < ntiles) load_tile(vrs, Vs(Other{}), (j + 1) * BC);
+  };
+  // the loads of this iteration have landed in LDS and every wave is done with this tile
+  auto publish = [&]() {
+    wait_all_loads();
+    __syncthreads();
+  };
+
+  // One key tile j, software-pipelined: S^T of tile j is already in sc (computed one iteration
+  // earlier).  After the row maxima and the (rare) rescale, one basic block holds the MFMAs of
+  // S^T for tile j + 1 (into sn), the exponentials of tile j and its O^T += V^T P^T, so the
+  // scheduler overlaps matrix and vector work.  MASK selects the variant with causal / key-tail
+  // masking.
+  f32x16_t sA[QB][KB], sB[QB][KB];   // S^T of even / odd tiles
+  auto body = [&](int j, auto par, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(par)::value;
+    using Other = std::integral_constant<int, 1 - P>;
+    auto& sc = P == 0 ? sA : sB;
+    auto& sn = P == 0 ? sB : sA;
+    const int kt0 = j * BC;
+    stage(j, par);
+    // ---- row maxima of tile j; rescale when a row's maximum has grown by more than kStaleMax
+    float muse[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if constexpr (MASK) {
-          const int qrow = qw + 32 * qb + l32;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-              if (key >= N || (CAUSAL && key > qrow)) s[qb][kb][r] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        const float mt = max_halves(mx) * c;
-        // The accumulator is rescaled only when some row's maximum has grown by more than
-        // kStaleMax (log2 units) since the last rescale; otherwise the stale maximum is kept,
-        // probabilities stay <= 2^kStaleMax, and the final division by l (computed against the
-        // same maximum) gives the same result.
-        // The decision is per row (alpha is exactly 1 where the row keeps its maximum), so a
-        // row's result never depends on other rows; the branch only skips the multiplies when
-        // no row of the wave needs them.
-        const bool grow = mt > m[qb] + kStaleMax;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-          float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - mt) : 1.f;
-          // an opaque (volatile) definition of alpha pins the multiplies below inside this
-          // branch; left alone, the compiler hoists them and runs them on every tile
-          asm volatile("" : "+v"(alpha));
-          m[qb] = grow ? mt : m[qb];
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-        }
-        const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
-        float rs = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (MASK) {
+        const int qrow = qw + 32 * qb + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[qb][kb][r] * c - muse);
-            s[qb][kb][r] = p;
-            rs += p;
+            const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (CAUSAL && key > qrow)) sc[qb][kb][r] = -INFINITY;
           }
-        l[qb] += rs;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          pf[qb][kb][0] = pack8<BF16>(s[qb][kb], 0);
-          pf[qb][kb][1] = pack8<BF16>(s[qb][kb], 8);
-        }
       }
-      // ---- O^T += V^T P^T
-      const int G16 = lane >> 4, li = lane & 15;
+      float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int krow = 32 * kb + 16 * t + 4 * (G16 >> 1) + (li >> 2);
+        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[qb][kb][r]);
+      const float mt = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * c;
+      // The accumulator is rescaled only when some row's maximum has grown by more than
+      // kStaleMax (log2 units) since the last rescale; otherwise the stale maximum is kept,
+      // probabilities stay <= 2^kStaleMax, and the final division by l (computed against the
+      // same maximum) gives the same result.  The decision is per row (alpha is exactly 1
+      // where the row keeps its maximum), so a row's result never depends on other rows; the
+      // branch only skips the multiplies when no row of the wave needs them.
+      const bool grow = mt > m[qb] + kStaleMax;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - mt) : 1.f;
+        // an opaque (volatile) definition of alpha pins the multiplies inside this branch
+        asm volatile("" : "+v"(alpha));
+        m[qb] = grow ? mt : m[qb];
+        l[qb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int col = 32 * db + 16 * (G16 & 1) + 4 * (li & 3);
-            const i16x4_t lo = ds_read_tr16(Vb + krow * VSTR + col);
-            const i16x4_t hi = ds_read_tr16(Vb + (krow + 8) * VSTR + col);
-            const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32x32x16<BF16>(a, pf[qb][kb][t], o[qb][db]);
-          }
-        }
+        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+      }
+      muse[qb] = (m[qb] == -INFINITY) ? 0.f : m[qb];
     }
-
-    if (has_next) store_tile((j + 1) & 1);
-    __syncthreads();
+    // ---- S^T of the next tile (past the wave's last tile it reads a stale buffer and the
+    // result is never used), probabilities of tile j, O^T += V^T P^T
+    compute_s(Other{}, sn);
+    i16x8_t pf[QB][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sc[qb][kb][r] * c - muse[qb]);
+          sc[qb][kb][r] = p;
+          rs4[r & 3] += p;
+        }
+      l[qb] += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        pf[qb][kb][0] = pack8<BF16>(sc[qb][kb], 0);
+        pf[qb][kb][1] = pack8<BF16>(sc[qb][kb], 8);
+      }
+    }
+    const short* Vb = Vs(par);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int rb = (32 * kb + 16 * t) * D;   // 16 | row offset keeps the swizzle unchanged
+          const i16x4_t lo = ds_read_tr16(Vb + rb + off_v[db][0]);
+          const i16x4_t hi = ds_read_tr16(Vb + rb + off_v[db][1]);
+          const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32x32x16<BF16>(a, pf[qb][kb][t], o[qb][db]);
+        }
+    publish();
+  };
+  // staging only, for tiles this wave skips
+  auto idle = [&](int j) {
+    if (j & 1) stage(j, Par1{});
+    else stage(j, Par0{});
+    publish();
   };
 
-  load_tile(0);
-  store_tile(0);
+  // prologue: K_0, V_0, K_1 staged; S^T of tile 0
+  load_tile(krs, Ks(Par0{}), 0);
+  load_tile(vrs, Vs(Par0{}), 0);
+  if (ntiles > 1) load_tile(krs, Ks(Par1{}), BC);
+  publish();
+  if (jact > 0) compute_s(Par0{}, sA);
+  // the first iteration overwrites K buffer 0
   __syncthreads();
 
   // tiles [0, jmask) need no masking for any wave of the workgroup
-  const int jmask = min(ntiles, CAUSAL ? min(q0, N) / BC : N / BC);
+  const int jmask = min(jact, CAUSAL ? min(q0, N) / BC : N / BC);
   int j = 0;
-  for (; j < jmask; ++j) tile(j, std::false_type{});
-  for (; j < ntiles; ++j) tile(j, std::true_type{});
+  for (; j + 2 <= jmask; j += 2) {
+    body(j, Par0{}, std::false_type{});
+    body(j + 1, Par1{}, std::false_type{});
+  }
+  if (j < jmask) {
+    body(j, Par0{}, std::false_type{});
+    ++j;
+  }
+  for (; j < jact; ++j) {
+    if (j & 1) body(j, Par1{}, std::true_type{});
+    else body(j, Par0{}, std::true_type{});
+  }
+  for (; j < ntiles; ++j) idle(j);
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
 #pragma unroll
@@ -280,11 +337,8 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
   constexpr int BR = 4 * QB * 32;
   const int nqb = (N + BR - 1) / BR;
   const int BH = B * Hq;
-  const size_t lds = FwdTile<D, BC>::BYTES;
   auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
+  hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e);
   return hipGetLastError();
 }
