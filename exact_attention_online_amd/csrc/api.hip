@@ -12,8 +12,8 @@
 namespace eao {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
-hipError_t launch_bwd_pre(const void* o, const void* dout, int B, int Hq, int N, int d, bool bf16, void* workspace,
-                          hipStream_t stream);
+hipError_t launch_bwd_pre(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
+                          int d, bool bf16, void* workspace, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
                            const void* workspace, hipStream_t stream);
@@ -105,11 +105,12 @@ static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int
   return ATTN_OK;
 }
 
-int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int d, int dtype,
-                        void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({o, dout}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
+int attn_bwd_preprocess(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
+                        int N, int d, int dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, o, dout, lse}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  return eao::launch_bwd_pre(o, dout, B, Hq, N, d, dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
+  return eao::launch_bwd_pre(q, o, dout, lse, B, Hq, N, d, dtype == ATTN_BF16, workspace, (hipStream_t)stream) ==
+                 hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -143,7 +144,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st != ATTN_OK) return st;
   const bool bf16 = dtype == ATTN_BF16;
   const hipStream_t s = (hipStream_t)stream;
-  if (eao::launch_bwd_pre(o, dout, B, Hq, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (eao::launch_bwd_pre(q, o, dout, lse, B, Hq, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
   if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
                            s) != hipSuccess)
     return ATTN_ERR_HIP;

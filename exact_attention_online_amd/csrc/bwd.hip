@@ -8,18 +8,24 @@
 //   dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three kernels on the caller's stream, none of them atomic:
-//   1. bwd_pre: D = rowsum(dO * O) in fp32 (the workspace).
+//   1. bwd_pre: per query row D = rowsum(dO * O) and LSE * log2(e), and the 64-row tiles of Q
+//      and dO written transposed ([d][64 rows], see the workspace layout below), all in the
+//      caller's workspace.
 //   2. bwd_dkdv: one workgroup per (batch, K/V head, block of 128 keys); each of the 4 waves
 //      owns 32 keys and keeps their K and V fragments and its dK^T, dV^T accumulators in
 //      registers for the whole kernel.  The workgroup walks every query head of the K/V head's
-//      group and every block of 64 query rows (causal: from the diagonal on), so dK and dV are
-//      summed over the group in registers.  Q and dO tiles (plus LSE and D) are prefetched into
-//      registers one block ahead and stored into double-buffered swizzled LDS.  Per block:
+//      group and every tile of 64 query rows (causal: from the diagonal on), so dK and dV are
+//      summed over the group in registers.  The tiles of Q, dO, Q^T and dO^T go straight from
+//      HBM into double-buffered LDS (direct buffer -> LDS loads, one tile ahead), LSE and D into
+//      registers.  Per tile, in two halves of 32 rows:
 //        S = Q K^T, dP = dO V^T   (A = Q / dO rows via ds_read_b128, B = K / V registers; a lane
 //                                  owns one key column of the accumulator)
-//        P = exp2(S * scale * log2e - LSE * log2e) (causal mask on the diagonal blocks only);
+//        P = exp2(S * scale * log2e - LSE * log2e) (causal mask on the diagonal tiles only);
 //        dS = P * (dP - D);  dV^T += dO^T P, dK^T += Q^T dS with P and dS taken straight from
-//        the accumulators (dO^T, Q^T via ds_read_b64_tr_b16).
+//        the accumulators and dO^T, Q^T read as rows of the transposed tiles (ds_read_b128).
+//      Every LDS read is a 16-byte row read: the transposed copies cost one extra pass over Q
+//      and dO in the preprocess but halve the LDS instructions of the two transposed operands,
+//      and LDS instruction issue is what limits this kernel.
 //   3. bwd_dq: one workgroup per (batch, query head, block of 128 query rows), shaped like the
 //      forward: a lane owns one query row, so LSE and D are one register each.  Per key tile:
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T,
@@ -39,65 +45,140 @@
 namespace eao {
 
 constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup (32 per wave)
-constexpr int kBwdRows = 64;    // query rows per dK/dV step
+constexpr int kBwdRows = 64;    // query rows per dK/dV step (one tile)
 constexpr int kDqRows = 128;    // query rows per dQ workgroup (32 per wave)
 constexpr int kDqKeys = 64;     // keys per dQ step
 
+// Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256),
+// T = B * Hq * Npad * d * 2:
+//   [0, A)           D     float  [B*Hq][Npad]   rowsum(dO * O); 0 past N
+//   [A, 2A)          LSE2  float  [B*Hq][Npad]   LSE * log2(e); +inf past N
+//   [2A, 2A + T)     Q^T   16-bit [B*Hq][Npad/64][d][64]
+//   [2A + T, 2A+2T)  dO^T  16-bit [B*Hq][Npad/64][d][64]
+// Within each 64-row tile of Q^T / dO^T, row d holds the tile's 64 values of column d with the
+// queries of every group of 16 permuted (position 8g + e holds query 8(e/4) + 4g + e%4): a
+// 16-byte read at position 8g then matches the order in which an MFMA accumulator holds the
+// probabilities, so the transposed operands of dV and dK are plain row reads.
+struct BwdWs {
+  float* dsum;
+  float* lse2;
+  uint16_t* qt;
+  uint16_t* dot;
+  int npad;
+};
+
+static BwdWs bwd_ws(void* workspace, int B, int Hq, int N, int d) {
+  BwdWs w;
+  w.npad = (N + kBwdRows - 1) / kBwdRows * kBwdRows;
+  const size_t a = ((size_t)B * Hq * w.npad * 4 + 255) / 256 * 256;
+  const size_t t = (size_t)B * Hq * w.npad * d * 2;
+  char* base = (char*)workspace;
+  w.dsum = (float*)base;
+  w.lse2 = (float*)(base + a);
+  w.qt = (uint16_t*)(base + 2 * a);
+  w.dot = (uint16_t*)(base + 2 * a + t);
+  return w;
+}
+
 size_t bwd_workspace_bytes(int B, int Hq, int N, int d) {
-  (void)d;
-  return (((size_t)B * Hq * N * 4 + 255) / 256) * 256;
+  const size_t npad = (size_t)(N + kBwdRows - 1) / kBwdRows * kBwdRows;
+  const size_t a = ((size_t)B * Hq * npad * 4 + 255) / 256 * 256;
+  return 2 * a + 2 * (size_t)B * Hq * npad * d * 2;
 }
 
 // ------------------------------------------------------------------ 1. preprocess
-// 16 lanes per row; each lane handles D/16 of the row's elements.
+// One workgroup per (batch * query head, 64-row tile): D and LSE2 of the tile's rows, and the
+// tile of Q and of dO written transposed (through padded LDS).  Rows past N are zeros.
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ Dsum, size_t rows) {
-  constexpr int LPR = 16;                 // lanes per row
-  constexpr int EPL = D / LPR;            // elements per lane (8 for d = 128, 4 for d = 64)
-  const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                                                      float* __restrict__ Dsum, float* __restrict__ Lse2,
+                                                      uint16_t* __restrict__ QT, uint16_t* __restrict__ dOT, int N,
+                                                      int npad) {
+  constexpr int STR = D + 8;                 // padded LDS row (16-bit elements)
+  constexpr int CPT = D / 32;                // 16-byte chunks per thread per row (4 threads per row)
+  __shared__ uint16_t tq[kBwdRows * STR], tdo[kBwdRows * STR];
+  const int ntile = npad / kBwdRows;
+  const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
+  const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+  const int q = tile * kBwdRows + row;
+  const size_t src = ((size_t)bh * N + q) * D + part * (D / 4);
   float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* op = O + row * D + sub * EPL;
-    const uint16_t* dp = dO + row * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc += to_float<BF16>(op[e]) * to_float<BF16>(dp[e]);
+  for (int cidx = 0; cidx < CPT; ++cidx) {
+    uint4 qv = {0, 0, 0, 0}, ov = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
+    if (q < N) {
+      qv = *(const uint4*)(Q + src + 8 * cidx);
+      ov = *(const uint4*)(O + src + 8 * cidx);
+      dv = *(const uint4*)(dO + src + 8 * cidx);
+    }
+    const uint16_t* o16 = (const uint16_t*)&ov;
+    const uint16_t* d16 = (const uint16_t*)&dv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += to_float<BF16>(o16[e]) * to_float<BF16>(d16[e]);
+    *(uint4*)(tq + row * STR + part * (D / 4) + 8 * cidx) = qv;
+    *(uint4*)(tdo + row * STR + part * (D / 4) + 8 * cidx) = dv;
   }
+  acc += __shfl_xor(acc, 1, 4);
+  acc += __shfl_xor(acc, 2, 4);
+  if (part == 0) {
+    const size_t r = (size_t)bh * npad + q;
+    Dsum[r] = q < N ? acc : 0.f;
+    Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  }
+  __syncthreads();
+  // transposed tile [D][64]: thread -> column d, 8-position groups of that row
+  constexpr int TPD = 256 / D;               // threads per transposed row
+  constexpr int GPT = 8 / TPD;               // 8-position groups per thread
+  const int d = tid / TPD, sub = tid % TPD;
+  const size_t dst = (((size_t)bh * ntile + tile) * D + d) * kBwdRows;
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && sub == 0) Dsum[row] = acc;
+  for (int gi = 0; gi < GPT; ++gi) {
+    const int p0 = 8 * (sub * GPT + gi);     // first position of the group
+    uint16_t vq[8], vd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pp = p0 + e;                 // position within the tile row
+      const int k = pp & 15;                 // slot 8g + e' within its 16-group
+      const int qq = (pp & ~15) + 8 * ((k & 7) >> 2) + 4 * (k >> 3) + (k & 3);
+      vq[e] = tq[qq * STR + d];
+      vd[e] = tdo[qq * STR + d];
+    }
+    *(uint4*)(QT + dst + p0) = *(const uint4*)vq;
+    *(uint4*)(dOT + dst + p0) = *(const uint4*)vd;
+  }
 }
 
 // ------------------------------------------------------------------ 2. dK, dV
-// LDS: Q, dO tiles [64 rows][D] double buffered with XOR-swizzled 16-byte chunks (read row-wise
-// with ds_read_b128 and transposed with ds_read_b64_tr_b16; the lane-dependent offsets are
-// computed once), then float LSE*log2(e) and D for both buffers.
-template <int D>
-struct DkdvSmem {
-  static constexpr int TILE = kBwdRows * D;
-  static constexpr int Q_OFF(int buf) { return buf * 2 * TILE; }
-  static constexpr int DO_OFF(int buf) { return buf * 2 * TILE + TILE; }
-  static constexpr int F_OFF = 4 * TILE;
-  static constexpr size_t BYTES = (size_t)F_OFF * 2 + 2 * 2 * kBwdRows * 4;
-};
-
+// Per step (one 64-row query tile): four tiles in LDS, double-buffered, each a distinct LDS
+// object so that direct loads into one buffer never make the compiler wait before reads of the
+// other: [Q | dO] ([64 rows][D], chunks XOR-swizzled by swz) and [Q^T | dO^T] ([D rows][64],
+// chunk c of row r at c ^ ((r / 2) % 8)).  Every operand is read with ds_read_b128; the tiles
+// are filled by direct buffer -> LDS loads (no staging registers, no LDS write instructions).
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int nkb,
-    float c /* scale * log2(e) */, float scale) {
-  using SM = DkdvSmem<D>;
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
+    const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int npad, int nkb, float c /* scale * log2(e) */,
+    float scale) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
-  constexpr int NLD = kBwdRows * CH / 256;          // 16-byte chunks per thread per tile
-  extern __shared__ uint4 smem_u4[];
-  short* sm = (short*)smem_u4;
-  float* smf = (float*)(sm + SM::F_OFF);            // [buf][0: LSE2 | 1: D][64]
+  constexpr int TILE = kBwdRows * D;                // 16-bit elements per tile
+  constexpr int PIECES = TILE * 2 / 1024;           // 1 KB direct-load pieces per tile
+  static_assert(PIECES % 4 == 0, "each wave moves the same number of pieces");
+  __shared__ __attribute__((aligned(1024))) short qd0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) short qd1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) short tt0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) short tt1[2 * TILE];
+  auto QD = [&](auto par) -> short* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return qd0; else return qd1;
+  };
+  auto TT = [&](auto par) -> short* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return tt0; else return tt1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int G16 = lane >> 4, li = lane & 15;
   const int G = Hq / Hkv;
   // key block major: under causal masking the first key blocks see the most query rows, so
   // the heaviest workgroups of every head start first
@@ -129,165 +210,214 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dkacc[db] = f32x16_t{};
   }
 
-  const int nqb = (N + kBwdRows - 1) / kBwdRows;
+  const int nqb = npad / kBwdRows;
   const int qstart = CAUSAL ? (k0 / kBwdRows) : 0;
   const int per_head = nqb - qstart;
   const int total = G * per_head;
   // causal: only the first kBwdKeys / kBwdRows query blocks of every head cross the diagonal
   constexpr int kDiag = kBwdKeys / kBwdRows;
 
-  // lane-dependent LDS offsets (16-bit units), loop invariant
-  int off_row[KK];                 // A operand rows 32qs + l32, chunk 2kk + g (qs adds 32 rows)
+  // loop-invariant offsets.  Reads (16-bit units): Q / dO rows 32qs + l32 at chunk 2kk + g;
+  // Q^T / dO^T rows 32db + l32 at chunk 4qs + 2t + g.  Direct loads (bytes): piece 4i + w of
+  // a tile, lane l -> LDS chunk 64(4i + w) + l, fetched from the logical chunk the swizzle
+  // puts there.
+  int off_row[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) off_row[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
-  int off_tr[DB][2];               // transposed reads: rows 4(G16/2) + li/4 (+8), column block db
+  const int tsw = (l32 >> 1) & 7;
+  int off_t[2][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      off_tr[db][h] = elem_index<D>(4 * (G16 >> 1) + (li >> 2) + 8 * h, 32 * db + 16 * (G16 & 1) + 4 * (li & 3));
+    for (int t = 0; t < 2; ++t) off_t[qs][t] = l32 * kBwdRows + (((4 * qs + 2 * t + g) ^ tsw) << 3);
+  uint32_t dma_qd[PIECES / 4], dma_tt[PIECES / 4];
+#pragma unroll
+  for (int i = 0; i < PIECES / 4; ++i) {
+    const int pch = 64 * (4 * i + w) + lane;
+    const int r = pch / CH, cc = pch % CH;
+    dma_qd[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
+    const int rt = pch / 8, ct = pch % 8;
+    dma_tt[i] = ((uint32_t)rt * kBwdRows + ((ct ^ ((rt >> 1) & 7)) << 3)) * 2;
+  }
 
-  uint4 qreg[NLD], doreg[NLD];
-  float lse_reg = 0.f, d_reg = 0.f;
-  auto block_of = [&](int it, int& h, int& q0) {
+  auto block_of = [&](int it, int& h, int& q0) __attribute__((always_inline)) {
     const int hh = it / per_head;
     h = kvh * G + hh;
     q0 = (qstart + it - hh * per_head) * kBwdRows;
   };
-  auto load_tile = [&](int it) {
+  // direct loads of block it's four tiles into buffer `par`
+  auto load_tiles = [&](int it, auto par) __attribute__((always_inline)) {
     int h, q0;
     block_of(it, h, q0);
-    const size_t q_row0 = ((size_t)b * Hq + h) * (size_t)N;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + q_row0 * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + q_row0 * D, head_bytes);
+    const size_t bhq = (size_t)b * Hq + h;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + bhq * N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + bhq * N * D, head_bytes);
+    const size_t toff = (bhq * nqb + q0 / kBwdRows) * TILE;
+    const __amdgpu_buffer_rsrc_t qtrs = make_rsrc(QT + toff, TILE * 2);
+    const __amdgpu_buffer_rsrc_t otrs = make_rsrc(dOT + toff, TILE * 2);
+    short* qd = QD(par);
+    short* tt = TT(par);
+    const uint32_t rowoff = (uint32_t)q0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      const uint32_t off = ((uint32_t)(q0 + row) * D + ch * 8) * 2;
-      qreg[i] = buffer_load16(qrs, off);
-      doreg[i] = buffer_load16(ors, off);
-    }
-    if (tid < kBwdRows) {
-      const int q = q0 + tid;
-      lse_reg = q < N ? LSE[q_row0 + q] * kLog2e : 0.f;
-      d_reg = q < N ? Dsum[q_row0 + q] : 0.f;
+    for (int i = 0; i < PIECES / 4; ++i) {
+      const int piece = 4 * i + w;
+      buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + rowoff);
+      buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + rowoff);
+      buffer_load16_lds(qtrs, tt + 512 * piece, dma_tt[i]);
+      buffer_load16_lds(otrs, tt + TILE + 512 * piece, dma_tt[i]);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint4* qs = (uint4*)(sm + SM::Q_OFF(buf));
-    uint4* ds = (uint4*)(sm + SM::DO_OFF(buf));
+  // LSE2 and D of the 16 rows a lane needs in half qs of block it: rows 32qs + 8rr + 4g + e
+  auto load_stats = [&](int it, int qs, float4 (&l4)[4], float4 (&d4)[4]) __attribute__((always_inline)) {
+    int h, q0;
+    block_of(it, h, q0);
+    const size_t r0 = ((size_t)b * Hq + h) * npad + q0 + 32 * qs + 4 * g;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      qs[chunk_index<D>(row, ch)] = qreg[i];
-      ds[chunk_index<D>(row, ch)] = doreg[i];
-    }
-    if (tid < kBwdRows) {
-      smf[buf * 2 * kBwdRows + tid] = lse_reg;
-      smf[buf * 2 * kBwdRows + kBwdRows + tid] = d_reg;
+    for (int rr = 0; rr < 4; ++rr) {
+      l4[rr] = *(const float4*)(Lse2 + r0 + 8 * rr);
+      d4[rr] = *(const float4*)(Dsum + r0 + 8 * rr);
     }
   };
 
-  // One query block: S, dP, P, dS, dV, dK.
-  auto step = [&](int it, auto mask_tag) {
+  // S = Q K^T, dP = dO V^T for rows 32qs .. 32qs+31 of the tile in buffer `par`; a lane owns
+  // key kw + l32 of the accumulator, register r holds query 32qs + 8(r/4) + 4g + r%4
+  auto s_dp = [&](auto par, int qs, f32x16_t& sacc, f32x16_t& dp) __attribute__((always_inline)) {
+    const short* Qs = QD(par) + 32 * qs * D;
+    const short* dOs = QD(par) + TILE + 32 * qs * D;
+    sacc = f32x16_t{};
+    dp = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const i16x8_t aq = __builtin_bit_cast(i16x8_t, *(const uint4*)(Qs + off_row[kk]));
+      const i16x8_t ado = __builtin_bit_cast(i16x8_t, *(const uint4*)(dOs + off_row[kk]));
+      sacc = mfma32x32x16<BF16>(aq, kf[kk], sacc);
+      dp = mfma32x32x16<BF16>(ado, vf[kk], dp);
+    }
+  };
+  // P = exp2(S c - LSE2) and dS = P (dP - D), packed as the B operands of dV^T and dK^T
+  auto p_ds = [&](int q0, int qs, f32x16_t& sacc, f32x16_t& dp, const float4 (&l4)[4], const float4 (&d4)[4],
+                  i16x8_t (&pb)[2], i16x8_t (&sb)[2], auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = it & 1;
-    const bool has_next = it + 1 < total;
-    if (has_next) load_tile(it + 1);
-    int h, q0;
-    block_of(it, h, q0);
-    const short* Qs = sm + SM::Q_OFF(buf);
-    const short* dOs = sm + SM::DO_OFF(buf);
-    const float* lse_s = smf + buf * 2 * kBwdRows;
-    const float* d_s = lse_s + kBwdRows;
     const int key = kw + l32;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      // S = Q K^T, dP = dO V^T for rows 32qs .. 32qs+31 of the block
-      f32x16_t sacc = f32x16_t{}, dp = f32x16_t{};
+    for (int rr = 0; rr < 4; ++rr) {
+      const float lv[4] = {l4[rr].x, l4[rr].y, l4[rr].z, l4[rr].w};
+      const float dv4[4] = {d4[rr].x, d4[rr].y, d4[rr].z, d4[rr].w};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const i16x8_t aq = __builtin_bit_cast(i16x8_t, *(const uint4*)(Qs + 32 * qs * D + off_row[kk]));
-        const i16x8_t ado = __builtin_bit_cast(i16x8_t, *(const uint4*)(dOs + 32 * qs * D + off_row[kk]));
-        sacc = mfma32x32x16<BF16>(aq, kf[kk], sacc);
-        dp = mfma32x32x16<BF16>(ado, vf[kk], dp);
-      }
-      // scheduling hint: the LDS reads of the S/dP operands run two MFMA pairs ahead of their
-      // use (mask 0x100 = LDS reads, 0x008 = MFMA); left alone the compiler issues each read
-      // right before its MFMA and the single wave per SIMD waits out every LDS latency
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2, 0);
-#pragma unroll
-      for (int i = 0; i < KK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      // P and dS; lane owns key kw + l32, register r holds query q0 + 32qs + 8(r/4) + 4g + r%4
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int qr = 32 * qs + 8 * rr + 4 * g;
-        const float4 l4 = *(const float4*)(lse_s + qr);
-        const float4 d4 = *(const float4*)(d_s + qr);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rr + e;
-          float p = __builtin_amdgcn_exp2f(sacc[r] * c - lv[e]);
-          if constexpr (MASK) {
-            if (key > q0 + qr + e) p = 0.f;
-          }
-          sacc[r] = p;
-          dp[r] = p * (dp[r] - dv4[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rr + e;
+        float p = __builtin_amdgcn_exp2f(sacc[r] * c - lv[e]);
+        if constexpr (MASK) {
+          if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
         }
-      }
-      const i16x8_t pb[2] = {pack8<BF16>(sacc, 0), pack8<BF16>(sacc, 8)};
-      const i16x8_t sb[2] = {pack8<BF16>(dp, 0), pack8<BF16>(dp, 8)};
-      // dV^T += dO^T P ; dK^T += Q^T dS   (k = query rows, slot (g, e) as in the forward)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int rbase = (32 * qs + 16 * t) * D;   // 16 | row offset keeps the swizzle unchanged
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const i16x4_t a0 = ds_read_tr16(dOs + rbase + off_tr[db][0]);
-          const i16x4_t a1 = ds_read_tr16(dOs + rbase + off_tr[db][1]);
-          const i16x8_t ado = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          dvacc[db] = mfma32x32x16<BF16>(ado, pb[t], dvacc[db]);
-          const i16x4_t b0 = ds_read_tr16(Qs + rbase + off_tr[db][0]);
-          const i16x4_t b1 = ds_read_tr16(Qs + rbase + off_tr[db][1]);
-          const i16x8_t aq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          dkacc[db] = mfma32x32x16<BF16>(aq, sb[t], dkacc[db]);
-        }
-      }
-      // scheduling hint: the transposed reads of dO^T / Q^T run two MFMA pairs ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * 2, 1);
-#pragma unroll
-      for (int i = 0; i < 2 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        sacc[r] = p;
+        dp[r] = p * (dp[r] - dv4[e]);
       }
     }
-    if (has_next) store_tile(buf ^ 1);
-    // one barrier per block: the next tile becomes visible and every wave is done with the
-    // buffer the block after overwrites
+    pb[0] = pack8<BF16>(sacc, 0);
+    pb[1] = pack8<BF16>(sacc, 8);
+    sb[0] = pack8<BF16>(dp, 0);
+    sb[1] = pack8<BF16>(dp, 8);
+  };
+  // dV^T += dO^T P, dK^T += Q^T dS for rows 32qs .. (k = query rows 32qs + 16t + slot order)
+  auto dv_dk = [&](auto par, int qs, const i16x8_t (&pb)[2], const i16x8_t (&sb)[2]) __attribute__((always_inline)) {
+    const short* tq = TT(par);
+    const short* tdo = TT(par) + TILE;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o = 32 * db * kBwdRows + off_t[qs][t];
+        const i16x8_t ado = __builtin_bit_cast(i16x8_t, *(const uint4*)(tdo + o));
+        dvacc[db] = mfma32x32x16<BF16>(ado, pb[t], dvacc[db]);
+        const i16x8_t aq = __builtin_bit_cast(i16x8_t, *(const uint4*)(tq + o));
+        dkacc[db] = mfma32x32x16<BF16>(aq, sb[t], dkacc[db]);
+      }
+    }
+  };
+
+  // One query block (tile in buffer `par`).  The statistics of half 0 were loaded during the
+  // previous step; those of half 1 are requested before the next block's tiles, so waiting for
+  // them never waits for the tiles.  Within the block, the S/dP MFMAs of half 1 are independent
+  // of the P/dS vector work of half 0, and the dV/dK MFMAs of half 0 of the vector work of
+  // half 1, which lets the scheduler overlap them.
+  float4 la[4], da[4], lb[4], db4[4];
+  auto step = [&](int it, auto par, auto mask_tag) __attribute__((always_inline)) {
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    const bool has_next = it + 1 < total;
+    int h, q0;
+    block_of(it, h, q0);
+    load_stats(it, 1, lb, db4);
+    if (has_next) load_tiles(it + 1, Other{});
+    f32x16_t x0, x1, y0, y1;
+    i16x8_t pb0[2], sb0[2], pb1[2], sb1[2];
+    s_dp(par, 0, x0, x1);
+    p_ds(q0, 0, x0, x1, la, da, pb0, sb0, mask_tag);
+    s_dp(par, 1, y0, y1);
+    p_ds(q0, 1, y0, y1, lb, db4, pb1, sb1, mask_tag);
+    dv_dk(par, 0, pb0, sb0);
+    // (on the last block this re-reads its own statistics: unused, and no branch splits the
+    // block of independent work)
+    load_stats(min(it + 1, total - 1), 0, la, da);
+    dv_dk(par, 1, pb1, sb1);
+    // scheduling: LDS reads run 4 ahead of their MFMAs (mask 0x100 = LDS reads, 0x008 = MFMA,
+    // 0x402 = vector ALU); the P/dS vector work of each half sits between the MFMAs of the next
+    // contraction
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // block it + 1 has landed and every wave is done with this block's buffers
+    wait_all_loads();
     __syncthreads();
   };
 
   if (total > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_stats(0, 0, la, da);
+    load_tiles(0, Par0{});
   }
+  wait_all_loads();
   __syncthreads();
   int it = 0;
+  // steps [it, end) with the buffer parity of each step fixed at compile time
+  auto run = [&](int end, auto mask_tag) __attribute__((always_inline)) {
+    if ((it & 1) && it < end) {
+      step(it, Par1{}, mask_tag);
+      ++it;
+    }
+    for (; it + 1 < end; it += 2) {
+      step(it, Par0{}, mask_tag);
+      step(it + 1, Par1{}, mask_tag);
+    }
+    if (it < end) {
+      step(it, Par0{}, mask_tag);
+      ++it;
+    }
+  };
   if constexpr (CAUSAL) {
     for (int hh = 0; hh < G; ++hh) {
       const int diag_end = min(hh * per_head + kDiag, (hh + 1) * per_head);
-      for (; it < diag_end; ++it) step(it, std::true_type{});
-      for (; it < (hh + 1) * per_head; ++it) step(it, std::false_type{});
+      for (; it < diag_end; ++it) {
+        if (it & 1) step(it, Par1{}, std::true_type{});
+        else step(it, Par0{}, std::true_type{});
+      }
+      run((hh + 1) * per_head, std::false_type{});
     }
   } else {
-    for (; it < total; ++it) step(it, std::false_type{});
+    run(total, std::false_type{});
   }
 
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
@@ -326,8 +456,8 @@ struct DqSmem {
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int BH, int nqb, float c /* scale * log2(e) */,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
+    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int npad, int BH, int nqb, float c /* scale * log2(e) */,
     float scale) {
   using SM = DqSmem<D>;
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32, KB = kDqKeys / 32;
@@ -366,8 +496,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     dof[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(ors, off));
   }
   // rows past the end: LSE = +inf gives P = 0
-  const float lse2 = qrow < N ? LSE[q_row0 + qrow] * kLog2e : INFINITY;
-  const float dd = qrow < N ? Dsum[q_row0 + qrow] : 0.f;
+  const float lse2 = qrow < N ? Lse2[(size_t)bh * npad + qrow] : INFINITY;
+  const float dd = qrow < N ? Dsum[(size_t)bh * npad + qrow] : 0.f;
   wait_all_loads();
 
   f32x16_t acc[DB];
@@ -484,9 +614,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 // ------------------------------------------------------------------ launchers
 template <bool BF16, int D>
-static hipError_t launch_pre_t(const void* o, const void* dout, size_t rows, void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     (const uint16_t*)o, (const uint16_t*)dout, (float*)workspace, rows);
+static hipError_t launch_pre_t(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
+                               void* workspace, hipStream_t stream) {
+  const BwdWs w = bwd_ws(workspace, B, Hq, N, D);
+  const unsigned grid = (unsigned)((size_t)B * Hq * (w.npad / kBwdRows));
+  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)q,
+                     (const uint16_t*)o, (const uint16_t*)dout, lse, w.dsum, w.lse2, w.qt, w.dot, N, w.npad);
   return hipGetLastError();
 }
 
@@ -494,14 +627,13 @@ template <bool BF16, int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
                                 hipStream_t stream) {
+  (void)lse;   // the probabilities use LSE * log2(e) from the workspace
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
   const int nkb = (N + kBwdKeys - 1) / kBwdKeys;
-  auto kern = bwd_dkdv_kernel<BF16, D, CAUSAL>;
-  const size_t lds = DkdvSmem<D>::BYTES;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nkb * B * Hkv), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)dout, lse, (const float*)workspace, (uint16_t*)dk,
-                     (uint16_t*)dv, Hq, Hkv, N, nkb, scale * kLog2e, scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(nkb * B * Hkv), dim3(256), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
+                     w.lse2, w.qt, w.dot, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e,
+                     scale);
   return hipGetLastError();
 }
 
@@ -509,6 +641,8 @@ template <bool BF16, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               void* dq, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
                               hipStream_t stream) {
+  (void)lse;
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
   const int nqb = (N + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
   auto kern = bwd_dq_kernel<BF16, D, CAUSAL>;
@@ -516,18 +650,17 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)dout, lse, (const float*)workspace, (uint16_t*)dq, Hq, Hkv,
-                     N, BH, nqb, scale * kLog2e, scale);
+                     (const uint16_t*)v, (const uint16_t*)dout, w.dsum, w.lse2, (uint16_t*)dq, Hq, Hkv, N, w.npad,
+                     BH, nqb, scale * kLog2e, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pre(const void* o, const void* dout, int B, int Hq, int N, int d, bool bf16, void* workspace,
-                          hipStream_t stream) {
-  const size_t rows = (size_t)B * Hq * N;
-  if (bf16) return d == 128 ? launch_pre_t<true, 128>(o, dout, rows, workspace, stream)
-                            : launch_pre_t<true, 64>(o, dout, rows, workspace, stream);
-  return d == 128 ? launch_pre_t<false, 128>(o, dout, rows, workspace, stream)
-                  : launch_pre_t<false, 64>(o, dout, rows, workspace, stream);
+hipError_t launch_bwd_pre(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
+                          int d, bool bf16, void* workspace, hipStream_t stream) {
+  if (bf16) return d == 128 ? launch_pre_t<true, 128>(q, o, dout, lse, B, Hq, N, workspace, stream)
+                            : launch_pre_t<true, 64>(q, o, dout, lse, B, Hq, N, workspace, stream);
+  return d == 128 ? launch_pre_t<false, 128>(q, o, dout, lse, B, Hq, N, workspace, stream)
+                  : launch_pre_t<false, 64>(q, o, dout, lse, B, Hq, N, workspace, stream);
 }
 
 #define EAO_DISPATCH(FN, ...)                                                                 \

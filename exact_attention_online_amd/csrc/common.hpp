@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace eao {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -31,6 +33,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef i16x4_t __attribute__((address_space(3))) lds_i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Compile-time parity tags of double-buffered loops (which LDS buffer a step uses).
+using Par0 = std::integral_constant<int, 0>;
+using Par1 = std::integral_constant<int, 1>;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // C += A * B on one 32x32x16 MFMA; BF16 selects bfloat16, otherwise fp16 operands.

@@ -50,8 +50,6 @@ struct FwdTile {
   static constexpr int PIECES = ELEMS * 2 / 1024;  // 1 KB direct-load pieces per tile
 };
 
-using Par0 = std::integral_constant<int, 0>;
-using Par1 = std::integral_constant<int, 1>;
 
 template <bool BF16, int D, int QB, int BC, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(

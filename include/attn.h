@@ -71,8 +71,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const float* q_descale, const float* k_descale, const float* v_descale,
              attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: D = rowsum(dO * O) as float [B,Hq,N] (linear in N;
- * no N x N buffer).  0 if the sizes are invalid. */
+/* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
+ * up to a multiple of 64: D = rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
+ * transposed copies of Q and dO in 64-row tiles, 16-bit [B,Hq,Npad,d] each, i.e.
+ * 2 * roundup(4 * B * Hq * Npad, 256) + 4 * B * Hq * Npad * d bytes.  0 if the sizes are
+ * invalid. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /* Backward pass of L = <O, dO> ("FlashAttention (NeurIPS 2022)" notes, "Backward -
@@ -92,11 +95,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
  * streams once preprocess is complete) produces exactly what attn_bwd produces; attn_bwd is
  * these three calls on one stream.
- *   attn_bwd_preprocess: D = rowsum(dO * O) into the workspace.
+ *   attn_bwd_preprocess: D = rowsum(dO * O), LSE * log2(e) and the transposed tiles of q and
+ *                        dout into the workspace.
  *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
  *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
  * Arguments mean what they mean for attn_bwd; each returns an attn_status_t. */
-int attn_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int d, int dtype,
+int attn_bwd_preprocess(const void* q, const void* o, const void* dout, const float* lse,
+                        int B, int Hq, int Hkv, int N, int d, int dtype,
                         void* workspace, size_t workspace_bytes, attn_stream_t stream);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
