@@ -47,7 +47,7 @@ def load():
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, sz, vp]
     lib.attn_bwd.restype = i
-    lib.attn_bwd_preprocess.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
+    lib.attn_bwd_preprocess.argtypes = [vp] * 5 + [i] * 6 + [vp, sz, vp]
     lib.attn_bwd_preprocess.restype = i
     lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, sz, vp]
     lib.attn_bwd_dkdv.restype = i
@@ -158,8 +158,8 @@ def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, betwee
     hook = between or (lambda i: None)
     causal, scale = int(bool(causal)), float(scale)
     hook(0)
-    _check(lib.attn_bwd_preprocess(_ptr(q), _ptr(o), _ptr(do), _ptr(lse), B, Hq, Hkv, N, d, dt, _ptr(workspace), wsb,
-                                   st))
+    _check(lib.attn_bwd_preprocess(_ptr(q), _ptr(k), _ptr(o), _ptr(do), _ptr(lse), B, Hq, Hkv, N, d, dt,
+                                   _ptr(workspace), wsb, st))
     hook(1)
     _check(lib.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
                              causal, scale, dt, _ptr(workspace), wsb, st))

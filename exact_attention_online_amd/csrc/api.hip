@@ -12,8 +12,8 @@
 namespace eao {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
-hipError_t launch_bwd_pre(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
-                          int d, bool bf16, void* workspace, hipStream_t stream);
+hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
+                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
                            const void* workspace, hipStream_t stream);
@@ -25,7 +25,7 @@ hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const in
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
                           const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N, int d,
                           bool causal, float scale, hipStream_t stream);
-size_t bwd_workspace_bytes(int B, int Hq, int N, int d);
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 }  // namespace eao
 
 namespace {
@@ -88,7 +88,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   if (check_sizes(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
-  return eao::bwd_workspace_bytes(B, Hq, N, d);
+  return eao::bwd_workspace_bytes(B, Hq, Hkv, N, d);
 }
 
 // Shared checks of the backward entry points (pointer list, sizes, scale, dtype, workspace).
@@ -101,16 +101,17 @@ static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int
   const int st = check_sizes(B, Hq, Hkv, N, d);
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
-  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, N, d)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
   return ATTN_OK;
 }
 
-int attn_bwd_preprocess(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
-                        int N, int d, int dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({q, o, dout, lse}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
+int attn_bwd_preprocess(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
+                        int Hq, int Hkv, int N, int d, int dtype, void* workspace, size_t workspace_bytes,
+                        attn_stream_t stream) {
+  const int st = check_bwd({q, k, o, dout, lse}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  return eao::launch_bwd_pre(q, o, dout, lse, B, Hq, N, d, dtype == ATTN_BF16, workspace, (hipStream_t)stream) ==
-                 hipSuccess
+  return eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, dtype == ATTN_BF16, workspace,
+                             (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -144,7 +145,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st != ATTN_OK) return st;
   const bool bf16 = dtype == ATTN_BF16;
   const hipStream_t s = (hipStream_t)stream;
-  if (eao::launch_bwd_pre(q, o, dout, lse, B, Hq, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
   if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
                            s) != hipSuccess)
     return ATTN_ERR_HIP;

@@ -46,7 +46,7 @@ namespace eao {
 
 constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup (32 per wave)
 constexpr int kBwdRows = 64;    // query rows per dK/dV step (one tile)
-constexpr int kDqRows = 128;    // query rows per dQ workgroup (32 per wave)
+constexpr int kDqRows = 256;    // query rows per dQ workgroup (8 waves x 32)
 constexpr int kDqKeys = 64;     // keys per dQ step
 
 // Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256),
@@ -55,7 +55,8 @@ constexpr int kDqKeys = 64;     // keys per dQ step
 //   [A, 2A)          LSE2  float  [B*Hq][Npad]   LSE * log2(e); +inf past N
 //   [2A, 2A + T)     Q^T   16-bit [B*Hq][Npad/64][d][64]
 //   [2A + T, 2A+2T)  dO^T  16-bit [B*Hq][Npad/64][d][64]
-// Within each 64-row tile of Q^T / dO^T, row d holds the tile's 64 values of column d with the
+//   [2A+2T, +Tk)     K^T   16-bit [B*Hkv][Npad/64][d][64], Tk = B * Hkv * Npad * d * 2
+// Within each 64-row tile of Q^T / dO^T / K^T, row d holds the tile's 64 values of column d with the
 // queries of every group of 16 permuted (position 8g + e holds query 8(e/4) + 4g + e%4): a
 // 16-byte read at position 8g then matches the order in which an MFMA accumulator holds the
 // probabilities, so the transposed operands of dV and dK are plain row reads.
@@ -64,6 +65,7 @@ struct BwdWs {
   float* lse2;
   uint16_t* qt;
   uint16_t* dot;
+  uint16_t* kt;
   int npad;
 };
 
@@ -77,30 +79,71 @@ static BwdWs bwd_ws(void* workspace, int B, int Hq, int N, int d) {
   w.lse2 = (float*)(base + a);
   w.qt = (uint16_t*)(base + 2 * a);
   w.dot = (uint16_t*)(base + 2 * a + t);
+  w.kt = (uint16_t*)(base + 2 * a + 2 * t);
   return w;
 }
 
-size_t bwd_workspace_bytes(int B, int Hq, int N, int d) {
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   const size_t npad = (size_t)(N + kBwdRows - 1) / kBwdRows * kBwdRows;
   const size_t a = ((size_t)B * Hq * npad * 4 + 255) / 256 * 256;
-  return 2 * a + 2 * (size_t)B * Hq * npad * d * 2;
+  return 2 * a + 2 * (size_t)B * Hq * npad * d * 2 + (size_t)B * Hkv * npad * d * 2;
 }
 
 // ------------------------------------------------------------------ 1. preprocess
-// One workgroup per (batch * query head, 64-row tile): D and LSE2 of the tile's rows, and the
-// tile of Q and of dO written transposed (through padded LDS).  Rows past N are zeros.
+// Row tile [64][D] in padded LDS (row stride STR) -> transposed tile [D][64] at dst, queries
+// (keys) permuted within each group of 16 as described with the workspace layout.
+template <int D, int STR>
+__device__ __forceinline__ void write_transposed(const uint16_t* t, uint16_t* __restrict__ dst, int tid) {
+  constexpr int TPD = 256 / D;               // threads per transposed row
+  constexpr int GPT = 8 / TPD;               // 8-position groups per thread
+  const int d = tid / TPD, sub = tid % TPD;
+#pragma unroll
+  for (int gi = 0; gi < GPT; ++gi) {
+    const int p0 = 8 * (sub * GPT + gi);     // first position of the group
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pp = p0 + e;                 // position within the tile row
+      const int k = pp & 15;                 // slot 8g + e' within its 16-group
+      const int r = (pp & ~15) + 8 * ((k & 7) >> 2) + 4 * (k >> 3) + (k & 3);
+      v[e] = t[r * STR + d];
+    }
+    *(uint4*)(dst + (size_t)d * kBwdRows + p0) = *(const uint4*)v;
+  }
+}
+
+// Workgroups [0, B*Hq*ntile): one (batch * query head, 64-row tile) each: D and LSE2 of the
+// tile's rows, and the tiles of Q and dO written transposed.  Workgroups after that: one
+// (batch * K/V head, 64-row tile) each, the tile of K written transposed.  Rows past N are
+// zeros.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                                                      float* __restrict__ Dsum, float* __restrict__ Lse2,
-                                                      uint16_t* __restrict__ QT, uint16_t* __restrict__ dOT, int N,
-                                                      int npad) {
+                                                      const uint16_t* __restrict__ K, float* __restrict__ Dsum,
+                                                      float* __restrict__ Lse2, uint16_t* __restrict__ QT,
+                                                      uint16_t* __restrict__ dOT, uint16_t* __restrict__ KT, int N,
+                                                      int npad, int nq_blocks) {
   constexpr int STR = D + 8;                 // padded LDS row (16-bit elements)
   constexpr int CPT = D / 32;                // 16-byte chunks per thread per row (4 threads per row)
   __shared__ uint16_t tq[kBwdRows * STR], tdo[kBwdRows * STR];
   const int ntile = npad / kBwdRows;
-  const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
   const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+  if ((int)blockIdx.x >= nq_blocks) {
+    const int idx = blockIdx.x - nq_blocks;
+    const int bkv = idx / ntile, tile = idx % ntile;
+    const int kr = tile * kBwdRows + row;
+    const size_t src = ((size_t)bkv * N + kr) * D + part * (D / 4);
+#pragma unroll
+    for (int cidx = 0; cidx < CPT; ++cidx) {
+      uint4 kv = {0, 0, 0, 0};
+      if (kr < N) kv = *(const uint4*)(K + src + 8 * cidx);
+      *(uint4*)(tq + row * STR + part * (D / 4) + 8 * cidx) = kv;
+    }
+    __syncthreads();
+    write_transposed<D, STR>(tq, KT + ((size_t)bkv * ntile + tile) * D * kBwdRows, tid);
+    return;
+  }
+  const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
   const int q = tile * kBwdRows + row;
   const size_t src = ((size_t)bh * N + q) * D + part * (D / 4);
   float acc = 0.f;
@@ -127,26 +170,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
   }
   __syncthreads();
-  // transposed tile [D][64]: thread -> column d, 8-position groups of that row
-  constexpr int TPD = 256 / D;               // threads per transposed row
-  constexpr int GPT = 8 / TPD;               // 8-position groups per thread
-  const int d = tid / TPD, sub = tid % TPD;
-  const size_t dst = (((size_t)bh * ntile + tile) * D + d) * kBwdRows;
-#pragma unroll
-  for (int gi = 0; gi < GPT; ++gi) {
-    const int p0 = 8 * (sub * GPT + gi);     // first position of the group
-    uint16_t vq[8], vd[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pp = p0 + e;                 // position within the tile row
-      const int k = pp & 15;                 // slot 8g + e' within its 16-group
-      const int qq = (pp & ~15) + 8 * ((k & 7) >> 2) + 4 * (k >> 3) + (k & 3);
-      vq[e] = tq[qq * STR + d];
-      vd[e] = tdo[qq * STR + d];
-    }
-    *(uint4*)(QT + dst + p0) = *(const uint4*)vq;
-    *(uint4*)(dOT + dst + p0) = *(const uint4*)vd;
-  }
+  const size_t dst = ((size_t)bh * ntile + tile) * D * kBwdRows;
+  write_transposed<D, STR>(tq, QT + dst, tid);
+  write_transposed<D, STR>(tdo, dOT + dst, tid);
 }
 
 // ------------------------------------------------------------------ 2. dK, dV
@@ -442,47 +468,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ 3. dQ
-// LDS per buffer: K tile [64 keys][D] with XOR-swizzled chunks (row reads for S^T and
-// transposed reads for dQ^T), V tile [64 keys][D] with rows padded by 16 bytes (row reads).
-template <int D>
-struct DqSmem {
-  static constexpr int KT = kDqKeys * D;
-  static constexpr int VSTR = D + 8;
-  static constexpr int VT = kDqKeys * VSTR;
-  static constexpr int BUF = KT + VT;
-  static constexpr size_t BYTES = (size_t)2 * BUF * 2;
-};
-
+// One workgroup of 8 waves per (batch, query head, block of 256 query rows); a wave owns 32
+// rows (two waves per SIMD).  Per key tile of 64, three tiles in double-buffered LDS, each pair
+// of buffers distinct LDS objects, filled by direct buffer -> LDS loads: [K | V] ([64][D],
+// chunks swizzled by swz) and K^T ([D][64] from the preprocess, chunk c of row r at
+// c ^ ((r / 2) % 8)).  All LDS reads are 16-byte rows.
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
-    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int npad, int BH, int nqb, float c /* scale * log2(e) */,
-    float scale) {
-  using SM = DqSmem<D>;
-  constexpr int CH = D / 8, KK = D / 16, DB = D / 32, KB = kDqKeys / 32;
-  constexpr int NLD = kDqKeys * CH / 256;
-  constexpr int VSTR = SM::VSTR;
-  extern __shared__ uint4 smem_u4[];
-  short* sm = (short*)smem_u4;
-  auto Ks = [&](int buf) { return sm + buf * SM::BUF; };
-  auto Vs = [&](int buf) { return sm + buf * SM::BUF + SM::KT; };
+    const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int npad, int BH, int nqb,
+    float c /* scale * log2(e) */, float scale) {
+  constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
+  constexpr int NW = kDqRows / 32;                  // waves per workgroup
+  constexpr int TILE = kDqKeys * D;                 // 16-bit elements per tile
+  constexpr int PIECES = TILE * 2 / 1024;           // 1 KB direct-load pieces per tile
+  static_assert(PIECES % NW == 0, "each wave moves the same number of pieces");
+  constexpr int PW = PIECES / NW;                   // pieces per wave per tile
+  __shared__ __attribute__((aligned(1024))) short kv0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) short kv1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) short kt0[TILE];
+  __shared__ __attribute__((aligned(1024))) short kt1[TILE];
+  auto KV = [&](auto par) -> short* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return kv0; else return kv1;
+  };
+  auto KTs = [&](auto par) -> short* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return kt0; else return kt1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int G16 = lane >> 4, li = lane & 15;
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
-  const size_t q_row0 = ((size_t)b * Hq + h) * (size_t)N;
-  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
+  const int bkv = b * Hkv + kvh;
+  const size_t q_row0 = (size_t)bh * N;
+  const size_t kv_off = (size_t)bkv * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + q_row0 * D, head_bytes);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + q_row0 * D, head_bytes);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
+  const int ntile_all = npad / kDqKeys;
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(KT + (size_t)bkv * ntile_all * TILE, (uint32_t)ntile_all * TILE * 2);
 
   const int q0 = qblk * kDqRows;
   const int qw = q0 + 32 * w;
@@ -504,97 +534,164 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
-  // lane-dependent K-tile offsets (16-bit units), loop invariant
-  int off_row[KK];                 // S^T A operand: rows 32kb + l32, chunk 2kk + g
+  // loop-invariant offsets.  Reads (16-bit units): K / V rows 32kb + l32 at chunk 2kk + g;
+  // K^T rows 32db + l32 at chunk 4kb + 2t + g.  Direct loads (bytes): piece NW i + w of a
+  // tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
+  int off_row[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) off_row[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
-  int off_tr[DB][2];               // K^T A operand: rows 4(G16/2) + li/4 (+8), column block db
+  const int tsw = (l32 >> 1) & 7;
+  int off_t[2][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      off_tr[db][hh] = elem_index<D>(4 * (G16 >> 1) + (li >> 2) + 8 * hh, 32 * db + 16 * (G16 & 1) + 4 * (li & 3));
+    for (int t = 0; t < 2; ++t) off_t[kb][t] = l32 * kDqKeys + (((4 * kb + 2 * t + g) ^ tsw) << 3);
+  uint32_t dma_kv[PW], dma_t[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int pch = 64 * (NW * i + w) + lane;
+    const int r = pch / CH, cc = pch % CH;
+    dma_kv[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
+    const int rt = pch / 8, ct = pch % 8;
+    dma_t[i] = ((uint32_t)rt * kDqKeys + ((ct ^ ((rt >> 1) & 7)) << 3)) * 2;
+  }
+  auto load_tiles = [&](int j, auto par) __attribute__((always_inline)) {
+    short* kv = KV(par);
+    short* kt = KTs(par);
+    const uint32_t rowoff = (uint32_t)j * kDqKeys * D * 2;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int piece = NW * i + w;
+      buffer_load16_lds(krs, kv + 512 * piece, dma_kv[i] + rowoff);
+      buffer_load16_lds(vrs, kv + TILE + 512 * piece, dma_kv[i] + rowoff);
+      buffer_load16_lds(trs, kt + 512 * piece, dma_t[i] + rowoff);
+    }
+  };
 
   const int kend = CAUSAL ? min(N, q0 + kDqRows) : N;
   const int ntiles = (kend + kDqKeys - 1) / kDqKeys;
-  uint4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int kt0) {
+  // a wave takes part in tiles [0, jact); under causal masking only tiles [jmask, jact) cross
+  // its diagonal
+  const int jact = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (qw + 31) / kDqKeys + 1) : ntiles);
+  const int jmask = CAUSAL ? min(jact, q0 / kDqKeys) : jact;
+
+  // S^T, dP^T for keys 32kb .. 32kb+31 of the tile in buffer `par`; lane owns query qrow,
+  // register r holds key 32kb + 8(r/4) + 4g + r%4
+  auto s_dp = [&](auto par, int kb, f32x16_t& st, f32x16_t& dpt) __attribute__((always_inline)) {
+    const short* Kb = KV(par) + 32 * kb * D;
+    const short* Vb = KV(par) + TILE + 32 * kb * D;
+    st = f32x16_t{};
+    dpt = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      const uint32_t off = ((uint32_t)(kt0 + row) * D + ch * 8) * 2;
-      kreg[i] = buffer_load16(krs, off);
-      vreg[i] = buffer_load16(vrs, off);
+    for (int kk = 0; kk < KK; ++kk) {
+      const i16x8_t ak = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + off_row[kk]));
+      const i16x8_t av = __builtin_bit_cast(i16x8_t, *(const uint4*)(Vb + off_row[kk]));
+      st = mfma32x32x16<BF16>(ak, qf[kk], st);
+      dpt = mfma32x32x16<BF16>(av, dof[kk], dpt);
     }
   };
-  auto store_tile = [&](int buf) {
+  // dS^T = P^T (dP^T - D), packed as the B operand of dQ^T
+  auto p_ds = [&](int kt0, int kb, f32x16_t& st, const f32x16_t& dpt, i16x8_t (&sb)[2],
+                  auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CH, ch = cidx % CH;
-      *(uint4*)(Ks(buf) + chunk_index<D>(row, ch) * 8) = kreg[i];
-      *(uint4*)(Vs(buf) + row * VSTR + ch * 8) = vreg[i];
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
+      if constexpr (MASK) {
+        if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
+      }
+      st[r] = p * (dpt[r] - dd);
     }
+    sb[0] = pack8<BF16>(st, 0);
+    sb[1] = pack8<BF16>(st, 8);
+  };
+  // dQ^T += K^T dS^T (slot (g, e) of half t is key 32kb + 16t + 8(e/4) + 4g + e%4)
+  auto dq_mma = [&](auto par, int kb, const i16x8_t (&sb)[2]) __attribute__((always_inline)) {
+    const short* kt = KTs(par);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(kt + 32 * db * kDqKeys + off_t[kb][t]));
+        acc[db] = mfma32x32x16<BF16>(a, sb[t], acc[db]);
+      }
   };
 
-  auto tile = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // One key tile j in buffer `par`: the S^T/dP^T MFMAs of the second 32 keys run beside the
+  // dS work of the first, the dQ MFMAs of the first beside the dS work of the second.
+  auto step = [&](int j, auto par, auto mask_tag) __attribute__((always_inline)) {
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    if (j + 1 < ntiles) load_tiles(j + 1, Other{});
     const int kt0 = j * kDqKeys;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(kt0 + kDqKeys);
-    const bool active = (qw < N) && (!CAUSAL || kt0 <= qw + 31);
-    if (active) {
-      const short* Kb = Ks(j & 1);
-      const short* Vb = Vs(j & 1);
+    f32x16_t s0, p0, s1, p1;
+    i16x8_t sb0[2], sb1[2];
+    s_dp(par, 0, s0, p0);
+    p_ds(kt0, 0, s0, p0, sb0, mask_tag);
+    s_dp(par, 1, s1, p1);
+    p_ds(kt0, 1, s1, p1, sb1, mask_tag);
+    dq_mma(par, 0, sb0);
+    dq_mma(par, 1, sb1);
+    // scheduling: LDS reads four ahead of their MFMAs (0x100 = LDS reads, 0x008 = MFMA,
+    // 0x402 = vector ALU)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        // S^T, dP^T for keys 32kb .. 32kb+31 of the tile
-        f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const i16x8_t ak = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + 32 * kb * D + off_row[kk]));
-          const i16x8_t av =
-              __builtin_bit_cast(i16x8_t, *(const uint4*)(Vb + (32 * kb + l32) * VSTR + 16 * kk + 8 * g));
-          st = mfma32x32x16<BF16>(ak, qf[kk], st);
-          dpt = mfma32x32x16<BF16>(av, dof[kk], dpt);
-        }
-        // dS^T; lane owns query qrow, register r holds key kt0 + 32kb + 8(r/4) + 4g + r%4
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
-          if constexpr (MASK) {
-            if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
-          }
-          st[r] = p * (dpt[r] - dd);
-        }
-        const i16x8_t sb[2] = {pack8<BF16>(st, 0), pack8<BF16>(st, 8)};
-        // dQ^T += K^T dS^T: slot (g, e) of half t is key 16t + 8(e/4) + 4g + e%4 (+32kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int rbase = (32 * kb + 16 * t) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const i16x4_t a0 = ds_read_tr16(Kb + rbase + off_tr[db][0]);
-            const i16x4_t a1 = ds_read_tr16(Kb + rbase + off_tr[db][1]);
-            const i16x8_t ak = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            acc[db] = mfma32x32x16<BF16>(ak, sb[t], acc[db]);
-          }
-        }
-      }
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    if (has_next) store_tile((j + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    wait_all_loads();
+    __syncthreads();
+  };
+  auto idle = [&](int j) __attribute__((always_inline)) {
+    if (j + 1 < ntiles) {
+      if (j & 1) load_tiles(j + 1, Par0{});
+      else load_tiles(j + 1, Par1{});
+    }
+    wait_all_loads();
     __syncthreads();
   };
 
-  load_tile(0);
-  store_tile(0);
+  load_tiles(0, Par0{});
+  wait_all_loads();
   __syncthreads();
-  // tiles [0, jmask) are wholly below the diagonal for every wave of the workgroup
-  const int jmask = CAUSAL ? min(ntiles, q0 / kDqKeys) : ntiles;
   int j = 0;
-  for (; j < jmask; ++j) tile(j, std::false_type{});
-  for (; j < ntiles; ++j) tile(j, std::true_type{});
+  auto run = [&](int end, auto mask_tag) __attribute__((always_inline)) {
+    if ((j & 1) && j < end) {
+      step(j, Par1{}, mask_tag);
+      ++j;
+    }
+    for (; j + 1 < end; j += 2) {
+      step(j, Par0{}, mask_tag);
+      step(j + 1, Par1{}, mask_tag);
+    }
+    if (j < end) {
+      step(j, Par0{}, mask_tag);
+      ++j;
+    }
+  };
+  run(jmask, std::false_type{});
+  for (; j < jact; ++j) {
+    if (j & 1) step(j, Par1{}, std::true_type{});
+    else step(j, Par0{}, std::true_type{});
+  }
+  for (; j < ntiles; ++j) idle(j);
 
   // epilogue: dQ = scale * dQ^T; register r of block db holds d = 32db + 8(r/4) + 4g + r%4
   if (qrow < N) {
@@ -614,12 +711,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 // ------------------------------------------------------------------ launchers
 template <bool BF16, int D>
-static hipError_t launch_pre_t(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
-                               void* workspace, hipStream_t stream) {
+static hipError_t launch_pre_t(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
+                               int Hq, int Hkv, int N, void* workspace, hipStream_t stream) {
   const BwdWs w = bwd_ws(workspace, B, Hq, N, D);
-  const unsigned grid = (unsigned)((size_t)B * Hq * (w.npad / kBwdRows));
+  const int ntile = w.npad / kBwdRows;
+  const int nq_blocks = B * Hq * ntile;
+  const unsigned grid = (unsigned)(nq_blocks + B * Hkv * ntile);
   hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)q,
-                     (const uint16_t*)o, (const uint16_t*)dout, lse, w.dsum, w.lse2, w.qt, w.dot, N, w.npad);
+                     (const uint16_t*)o, (const uint16_t*)dout, lse, (const uint16_t*)k, w.dsum, w.lse2, w.qt, w.dot,
+                     w.kt, N, w.npad, nq_blocks);
   return hipGetLastError();
 }
 
@@ -645,22 +745,18 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
   const int nqb = (N + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
-  auto kern = bwd_dq_kernel<BF16, D, CAUSAL>;
-  const size_t lds = DqSmem<D>::BYTES;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), lds, stream, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)dout, w.dsum, w.lse2, (uint16_t*)dq, Hq, Hkv, N, w.npad,
-                     BH, nqb, scale * kLog2e, scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
+                     w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pre(const void* q, const void* o, const void* dout, const float* lse, int B, int Hq, int N,
-                          int d, bool bf16, void* workspace, hipStream_t stream) {
-  if (bf16) return d == 128 ? launch_pre_t<true, 128>(q, o, dout, lse, B, Hq, N, workspace, stream)
-                            : launch_pre_t<true, 64>(q, o, dout, lse, B, Hq, N, workspace, stream);
-  return d == 128 ? launch_pre_t<false, 128>(q, o, dout, lse, B, Hq, N, workspace, stream)
-                  : launch_pre_t<false, 64>(q, o, dout, lse, B, Hq, N, workspace, stream);
+hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
+                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream) {
+  if (bf16) return d == 128 ? launch_pre_t<true, 128>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream)
+                            : launch_pre_t<true, 64>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream);
+  return d == 128 ? launch_pre_t<false, 128>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream)
+                  : launch_pre_t<false, 64>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream);
 }
 
 #define EAO_DISPATCH(FN, ...)                                                                 \

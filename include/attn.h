@@ -73,9 +73,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
  * up to a multiple of 64: D = rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
- * transposed copies of Q and dO in 64-row tiles, 16-bit [B,Hq,Npad,d] each, i.e.
- * 2 * roundup(4 * B * Hq * Npad, 256) + 4 * B * Hq * Npad * d bytes.  0 if the sizes are
- * invalid. */
+ * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and
+ * [B,Hkv,Npad,d] (K), i.e. 2 * roundup(4 * B * Hq * Npad, 256) + 2 * (2 * Hq + Hkv) * B * Npad * d
+ * bytes.  0 if the sizes are invalid. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /* Backward pass of L = <O, dO> ("FlashAttention (NeurIPS 2022)" notes, "Backward -
@@ -95,13 +95,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
  * streams once preprocess is complete) produces exactly what attn_bwd produces; attn_bwd is
  * these three calls on one stream.
- *   attn_bwd_preprocess: D = rowsum(dO * O), LSE * log2(e) and the transposed tiles of q and
- *                        dout into the workspace.
+ *   attn_bwd_preprocess: D = rowsum(dO * O), LSE * log2(e) and the transposed tiles of q,
+ *                        dout and k into the workspace.
  *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
  *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
  * Arguments mean what they mean for attn_bwd; each returns an attn_status_t. */
-int attn_bwd_preprocess(const void* q, const void* o, const void* dout, const float* lse,
-                        int B, int Hq, int Hkv, int N, int d, int dtype,
+int attn_bwd_preprocess(const void* q, const void* k, const void* o, const void* dout,
+                        const float* lse, int B, int Hq, int Hkv, int N, int d, int dtype,
                         void* workspace, size_t workspace_bytes, attn_stream_t stream);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,

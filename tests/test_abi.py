@@ -87,8 +87,8 @@ def test_workspace_is_linear_in_n():
     # and the transposed rows of Q and dO (d 16-bit values each) -- never an N x N buffer
     for n, s in zip((1024, 2048, 4096, 8192), sizes):
         rows = 2 * 8 * n
-        assert s == 2 * rows * 4 + 2 * rows * 128 * 2
+        assert s == 2 * rows * 4 + 2 * rows * 128 * 2 + 2 * 2 * n * 128 * 2   # Hkv = 2
     # rows are padded to whole tiles of 64
     assert ws(2, 8, 2, 1000, 128) == sizes[0]
-    assert ws(1, 1, 1, 65, 64) == 2 * 512 + 2 * 128 * 64 * 2
+    assert ws(1, 1, 1, 65, 64) == 2 * 512 + 3 * 128 * 64 * 2
     assert ws(2, 8, 3, 1024, 128) == 0 and ws(1, 1, 1, 1, 80) == 0
