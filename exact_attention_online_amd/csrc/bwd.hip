@@ -91,21 +91,20 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 
 // ------------------------------------------------------------------ 1. preprocess
 // Row tile [64][D] in padded LDS (row stride STR) -> transposed tile [D][64] at dst, queries
-// (keys) permuted within each group of 16 as described with the workspace layout.
+// (keys) permuted within each group of 16 as described with the workspace layout.  Eight
+// threads write one 128-byte row of the transposed tile.
 template <int D, int STR>
 __device__ __forceinline__ void write_transposed(const uint16_t* t, uint16_t* __restrict__ dst, int tid) {
-  constexpr int TPD = 256 / D;               // threads per transposed row
-  constexpr int GPT = 8 / TPD;               // 8-position groups per thread
-  const int d = tid / TPD, sub = tid % TPD;
+  const int p0 = 8 * (tid & 7);              // first position of this thread's group
 #pragma unroll
-  for (int gi = 0; gi < GPT; ++gi) {
-    const int p0 = 8 * (sub * GPT + gi);     // first position of the group
+  for (int k = 0; k < D / 32; ++k) {
+    const int d = (tid >> 3) + 32 * k;
     uint16_t v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pp = p0 + e;                 // position within the tile row
-      const int k = pp & 15;                 // slot 8g + e' within its 16-group
-      const int r = (pp & ~15) + 8 * ((k & 7) >> 2) + 4 * (k >> 3) + (k & 3);
+      const int s16 = pp & 15;               // slot 8g + e' within its 16-group
+      const int r = (pp & ~15) + 8 * ((s16 & 7) >> 2) + 4 * (s16 >> 3) + (s16 & 3);
       v[e] = t[r * STR + d];
     }
     *(uint4*)(dst + (size_t)d * kBwdRows + p0) = *(const uint4*)v;
@@ -115,7 +114,7 @@ __device__ __forceinline__ void write_transposed(const uint16_t* t, uint16_t* __
 // Workgroups [0, B*Hq*ntile): one (batch * query head, 64-row tile) each: D and LSE2 of the
 // tile's rows, and the tiles of Q and dO written transposed.  Workgroups after that: one
 // (batch * K/V head, 64-row tile) each, the tile of K written transposed.  Rows past N are
-// zeros.
+// zeros.  Loads: 16-byte chunk tid + 256 i of the tile, so each wave reads whole rows.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
@@ -124,50 +123,53 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
                                                       uint16_t* __restrict__ dOT, uint16_t* __restrict__ KT, int N,
                                                       int npad, int nq_blocks) {
   constexpr int STR = D + 8;                 // padded LDS row (16-bit elements)
-  constexpr int CPT = D / 32;                // 16-byte chunks per thread per row (4 threads per row)
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int CPT = kBwdRows * CH / 256;   // chunks per thread per tile
   __shared__ uint16_t tq[kBwdRows * STR], tdo[kBwdRows * STR];
   const int ntile = npad / kBwdRows;
-  const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+  const int tid = threadIdx.x;
   if ((int)blockIdx.x >= nq_blocks) {
     const int idx = blockIdx.x - nq_blocks;
     const int bkv = idx / ntile, tile = idx % ntile;
-    const int kr = tile * kBwdRows + row;
-    const size_t src = ((size_t)bkv * N + kr) * D + part * (D / 4);
+    const uint16_t* src = K + ((size_t)bkv * N + (size_t)tile * kBwdRows) * D;
 #pragma unroll
-    for (int cidx = 0; cidx < CPT; ++cidx) {
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
       uint4 kv = {0, 0, 0, 0};
-      if (kr < N) kv = *(const uint4*)(K + src + 8 * cidx);
-      *(uint4*)(tq + row * STR + part * (D / 4) + 8 * cidx) = kv;
+      if (tile * kBwdRows + row < N) kv = *(const uint4*)(src + (size_t)row * D + 8 * ch);
+      *(uint4*)(tq + row * STR + 8 * ch) = kv;
     }
     __syncthreads();
     write_transposed<D, STR>(tq, KT + ((size_t)bkv * ntile + tile) * D * kBwdRows, tid);
     return;
   }
   const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
-  const int q = tile * kBwdRows + row;
-  const size_t src = ((size_t)bh * N + q) * D + part * (D / 4);
-  float acc = 0.f;
+  const size_t base = ((size_t)bh * N + (size_t)tile * kBwdRows) * D;
 #pragma unroll
-  for (int cidx = 0; cidx < CPT; ++cidx) {
+  for (int i = 0; i < CPT; ++i) {
+    const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
+    const int q = tile * kBwdRows + row;
     uint4 qv = {0, 0, 0, 0}, ov = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
     if (q < N) {
-      qv = *(const uint4*)(Q + src + 8 * cidx);
-      ov = *(const uint4*)(O + src + 8 * cidx);
-      dv = *(const uint4*)(dO + src + 8 * cidx);
+      qv = *(const uint4*)(Q + base + (size_t)row * D + 8 * ch);
+      ov = *(const uint4*)(O + base + (size_t)row * D + 8 * ch);
+      dv = *(const uint4*)(dO + base + (size_t)row * D + 8 * ch);
     }
     const uint16_t* o16 = (const uint16_t*)&ov;
     const uint16_t* d16 = (const uint16_t*)&dv;
+    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += to_float<BF16>(o16[e]) * to_float<BF16>(d16[e]);
-    *(uint4*)(tq + row * STR + part * (D / 4) + 8 * cidx) = qv;
-    *(uint4*)(tdo + row * STR + part * (D / 4) + 8 * cidx) = dv;
-  }
-  acc += __shfl_xor(acc, 1, 4);
-  acc += __shfl_xor(acc, 2, 4);
-  if (part == 0) {
-    const size_t r = (size_t)bh * npad + q;
-    Dsum[r] = q < N ? acc : 0.f;
-    Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+    // the CH lanes holding one row are consecutive
+#pragma unroll
+    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
+    if (ch == 0) {
+      const size_t r = (size_t)bh * npad + q;
+      Dsum[r] = q < N ? acc : 0.f;
+      Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+    }
+    *(uint4*)(tq + row * STR + 8 * ch) = qv;
+    *(uint4*)(tdo + row * STR + 8 * ch) = dv;
   }
   __syncthreads();
   const size_t dst = ((size_t)bh * ntile + tile) * D * kBwdRows;
