@@ -9,6 +9,8 @@ Recipe (applies to every workload):
   * draw order: Q, K, V, then dO (only when a backward is asked for), each with
     ``standard_normal(shape, dtype=float32)``;
   * rounding to fp16/bf16 is round-to-nearest-even through torch's dtype conversion;
+  * decoding shapes (few query rows against a long key sequence): Q [B,Hq,Nq,d] then K, V
+    [B,Hkv,Nk,d], same generator and order;
   * fp8 extras (drawn after dO would be, from the same generator): for each of Q, K, V in that
     order, ``round(0.001 * numel)`` distinct flat indices chosen uniformly without replacement,
     whose entries are multiplied by 10 (outliers); then one sign vector of length d with entries
@@ -20,7 +22,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "draw", "draw_fp8", "round_to", "DTYPES"]
+__all__ = ["Workload", "WORKLOADS", "DECODE_WORKLOADS", "DecodeWorkload", "draw", "draw_decode", "draw_fp8",
+           "round_to", "DTYPES"]
 
 DTYPES = ("fp16", "bf16")
 
@@ -58,6 +61,42 @@ WORKLOADS = {
     "gqa_bf16": Workload("gqa_bf16", 4, 32, 8, 4096, 128, "bf16", True, True),
     "fp8": Workload("fp8", 4, 16, 16, 4096, 128, "fp8", False, False),
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decoding: Nq query rows per head against Nk keys (a K/V cache)."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+# One new token per sequence (Nq = 1) for 8 sequences of 32k cached keys, 32 query heads sharing
+# 8 K/V heads; and four tokens at once (speculative decoding) against 8k keys.
+DECODE_WORKLOADS = {
+    "decode_bf16": DecodeWorkload("decode_bf16", 8, 32, 8, 1, 32768, 128, "bf16", True),
+    "decode4_bf16": DecodeWorkload("decode4_bf16", 4, 32, 8, 4, 8192, 128, "bf16", True),
+}
+
+
+def draw_decode(B, Hq, Hkv, Nq, Nk, d, seed):
+    """Float32 Q [B,Hq,Nq,d], K, V [B,Hkv,Nk,d], N(0,1)."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    q = gen.standard_normal((B, Hq, Nq, d), dtype=np.float32)
+    k = gen.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = gen.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    return q, k, v
 
 
 def round_to(x: np.ndarray, dtype: str):

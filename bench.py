@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "decode_bf16", "decode4_bf16"],
+                    help="the headline fwd+bwd workload (default) or a split-KV decoding workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain device-to-device copy of MIB MiB (a kernel of "
                          "known traffic that scales HBM byte counters read under a profiler)")
@@ -105,6 +107,113 @@ def cpu_baseline(w, q, k, v, do, target_s):
     }
 
 
+def cpu_baseline_decode(w, q, k, v, target_s):
+    """The fp64 decoding oracle (as it stands) on whole (batch, K/V head) groups until target_s."""
+    from oracle import decode as DC
+
+    try:
+        import threadpoolctl
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    G = w.Hq // w.Hkv
+    t0 = time.perf_counter()
+    groups = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            DC.forward(q[b:b + 1, g * G:(g + 1) * G], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], w.causal, w.scale)
+            groups += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    kv_group = 2 * w.Nk * w.d * 2
+    return {
+        "value": round(kv_group * groups / el / 1e9, 6),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"fp64 forward of {groups} of {w.B * w.Hkv} (batch, K/V head) groups of the same workload "
+                  f"({G * w.Nq} query rows each), {el:.1f} s; rate counted as K+V bytes of the bf16 cache",
+    }
+
+
+def bench_decode(args):
+    """Split-KV decoding: K/V bytes streamed per second by attn_fwd_splitkv (split + merge kernels)."""
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import DECODE_WORKLOADS, draw_decode, round_to
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    w = DECODE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q32, k32, v32 = draw_decode(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, SEED)
+    qc, kc, vc = (round_to(x, w.dtype) for x in (q32, k32, v32))
+    del q32, k32, v32
+    q, k, v = (t.to(dev).contiguous() for t in (qc, kc, vc))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(eao.splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, 0), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(args.warmup):
+        eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse)
+    steps = max(args.steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        evs[i][0].record()
+        eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse)
+        evs[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    if not torch.isfinite(o).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+    kv_bytes = 2.0 * w.B * w.Hkv * w.Nk * w.d * 2
+    algo = kv_bytes + 2.0 * (2 * w.B * w.Hq * w.Nq * w.d) + 4.0 * w.B * w.Hq * w.Nq   # + Q read, O written, LSE
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "split-KV decoding: K/V cache GB/s streamed by attn_fwd_splitkv",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d} "
+                               f"causal={w.causal} fwd (split-KV)", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal, "seed": SEED, "pass": "fwd"},
+        "roofline": {
+            "kernel": "fwd_split_kernel<bf16, d=128> + fwd_split_merge_kernel (one attn_fwd_splitkv call)",
+            "bound": "hbm",
+            "achieved": round(algo / (ms_call * 1e-3) / 1e9, 1),
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": round(algo / (ms_call * 1e-3) / 1e9 / 8000.0, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, qc, kc, vc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -112,6 +221,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != WORKLOAD:
+        bench_decode(args)
+        return
 
     import torch
 

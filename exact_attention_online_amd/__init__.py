@@ -12,12 +12,13 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
-           "attn_bwd_dq", "attn_fp8_prep", "attn_status_string")
+           "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
+           "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -53,6 +54,10 @@ def load():
     lib.attn_bwd_dkdv.restype = i
     lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
+    lib.attn_fwd_splitkv_workspace_size.argtypes = [i] * 7
+    lib.attn_fwd_splitkv_workspace_size.restype = sz
+    lib.attn_fwd_splitkv.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, sz, vp]
+    lib.attn_fwd_splitkv.restype = i
     lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 4 + [vp]
     lib.attn_fp8_prep.restype = i
     lib.attn_status_string.argtypes = [i]
@@ -117,6 +122,40 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, dt, None, None, None, _stream(q.device)))
+    return out, lse
+
+
+def splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits=0) -> int:
+    return int(load().attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits))
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0, workspace=None,
+                out=None, lse=None):
+    """O, LSE for q [B,Hq,Nq,d] against k/v [B,Hkv,Nk,d] (Nq <= Nk) with the keys split among
+    workgroups (decoding); causal aligns the queries with the last Nq keys."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise AttnError(f"expected q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise AttnError("q and k/v disagree in B or d")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise AttnError("q, k, v must be contiguous device tensors of one dtype on one device")
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                   int(bool(causal)), scale, dt, int(num_splits), _ptr(workspace), wsb,
+                                   _stream(q.device)))
     return out, lse
 
 

@@ -26,6 +26,10 @@ hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, 
                           const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N, int d,
                           bool causal, float scale, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                              int Hkv, int Nq, int Nk, int d, bool causal, float scale, bool bf16, int num_splits,
+                              void* workspace, hipStream_t stream);
+size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 }  // namespace eao
 
 namespace {
@@ -153,6 +157,37 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
       hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+// Shapes of the split-KV forward: the rows sharing one K/V head (Hq / Hkv heads x Nq rows) must
+// fit one 32-row MFMA tile.
+static int check_splitkv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (Nq < 1 || Nk < 1 || num_splits < 0) return ATTN_ERR_INVALID;
+  const int st = check_sizes(B, Hq, Hkv, Nk, d);
+  if (st != ATTN_OK) return st;
+  if (Nq > Nk) return ATTN_ERR_INVALID;
+  if ((Hq / Hkv) * Nq > 32) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (check_splitkv(B, Hq, Hkv, Nq, Nk, d, num_splits) != ATTN_OK) return 0;
+  return eao::splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d, int causal, float softmax_scale, int dtype, int num_splits,
+                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  const int st = check_splitkv(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if (st != ATTN_OK) return st;
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)) return ATTN_ERR_WORKSPACE;
+  return eao::launch_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal != 0, softmax_scale,
+                                 dtype == ATTN_BF16, num_splits, workspace, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs, int B, int H, int N, int d,

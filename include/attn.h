@@ -111,6 +111,28 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
                 void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
                 int dtype, const void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* Split-KV forward for decoding ("FlashAttention-2: Faster Attention with Better Parallelism and
+ * Work Partitioning", OpenReview discussion: the author response on decoding and the review
+ * summary on splitting the KV cache among thread blocks to saturate memory bandwidth): few query
+ * rows per head against a long key/value sequence.  The keys of each (batch, K/V head) are cut
+ * into splits processed by separate workgroups; each split's exact partial result and logsumexp
+ * are combined by LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *   q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d]; o [B,Hq,Nq,d] in `dtype` (ATTN_F16 / ATTN_BF16);
+ *   lse [B,Hq,Nq] float, natural log.  Requires 1 <= Nq <= Nk and (Hq/Hkv) * Nq <= 32 (all rows
+ *   that share a K/V head fit one 32-row tile), else ATTN_ERR_UNSUPPORTED / ATTN_ERR_INVALID.
+ *   causal: query i sits at position Nk - Nq + i and sees keys j <= Nk - Nq + i (with Nq = 1
+ *   every key is visible).
+ *   num_splits: splits per (batch, K/V head), 0 = chosen for about two workgroups per compute
+ *   unit with splits of at least 1024 keys; clamped to the number of 128-key tiles.
+ *   workspace: device memory of at least attn_fwd_splitkv_workspace_size() bytes (the float
+ *   partial outputs and logsumexps of every split), 256-byte aligned, owned by the caller.
+ * Returns an attn_status_t. */
+size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                     int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                     attn_stream_t stream);
+
 /* FP8 preparation ("FlashAttention-3 ...", abstract: block quantisation and incoherent
  * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is
  * first replaced by (row * signs) H_d / sqrt(d), H_d the Sylvester Hadamard matrix, computed in

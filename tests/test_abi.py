@@ -92,3 +92,30 @@ def test_workspace_is_linear_in_n():
     assert ws(2, 8, 2, 1000, 128) == sizes[0]
     assert ws(1, 1, 1, 65, 64) == 2 * 512 + 3 * 128 * 64 * 2
     assert ws(2, 8, 3, 1024, 128) == 0 and ws(1, 1, 1, 1, 80) == 0
+
+
+def splitkv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128, causal=1, scale=0.1, dtype=1,
+             splits=0, ws=NULL, wsb=0)
+    a.update(kw)
+    return eao.load().attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                       a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], a["splits"], a["ws"],
+                                       a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(Nq=0), 1), (dict(Nq=1001), 1), (dict(splits=-1), 1), (dict(scale=0.0), 1),
+    (dict(dtype=2), 2), (dict(d=80), 2), (dict(Hq=8, Hkv=1, Nq=5), 2), (dict(Hq=3, Hkv=2), 1),
+    (dict(), 3), (dict(ws=P, wsb=16), 3),
+])
+def test_splitkv_rejects_bad_arguments(kw, code):
+    assert splitkv(**kw) == code
+
+
+def test_splitkv_workspace_size():
+    ws = eao.splitkv_workspace_size
+    # one split: partial O (float) and LSE of every row, each rounded up to 256 bytes
+    assert ws(1, 8, 2, 1, 100, 128, 1) == 8 * 128 * 4 + 256
+    # splits are clamped to the number of 128-key tiles and never empty
+    assert ws(1, 8, 2, 1, 300, 128, 64) == ws(1, 8, 2, 1, 300, 128, 3)
+    assert ws(1, 8, 1, 5, 100, 128, 0) == 0     # 8 heads x 5 rows do not fit one 32-row tile
