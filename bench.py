@@ -40,8 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "decode_bf16", "decode4_bf16"],
-                    help="the headline fwd+bwd workload (default) or a split-KV decoding workload")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16"],
+                    help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
+                         "shape's forward with a 4096-key sliding window and ALiBi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain device-to-device copy of MIB MiB (a kernel of "
                          "known traffic that scales HBM byte counters read under a profiler)")
@@ -214,6 +216,76 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_window(args):
+    """Forward of the long shape (B=1, H=16, N=16384, d=128, bf16, causal) with a 4096-key sliding
+    window and ALiBi slopes 2^(-8 h / H): TFLOP/s over the visible query-key pairs."""
+    import numpy as np
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import WORKLOADS, draw, round_to
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    w = WORKLOADS[WORKLOAD]
+    window = 4096
+    dev = torch.device("cuda:0")
+    _, q32, k32, v32, _ = draw(w.B, w.Hq, w.Hkv, w.N, w.d, SEED)
+    q, k, v = (round_to(x, w.dtype).to(dev).contiguous() for x in (q32, k32, v32))
+    del q32, k32, v32
+    slopes = torch.tensor(2.0 ** (-8.0 * np.arange(1, w.Hq + 1) / w.Hq), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        eao.fwd_ext(q, k, v, True, w.scale, window, slopes, o, lse)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        eao.fwd_ext(q, k, v, True, w.scale, window, slopes, o, lse)
+        evs[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    if not torch.isfinite(o).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+    pairs = sum(min(i + 1, window) for i in range(w.N))          # visible (query, key) pairs per head
+    flops = 4.0 * w.B * w.Hq * pairs * w.d
+    out = {
+        "metric": "attention fwd TFLOPs/s with a 4096-key sliding window and ALiBi (visible pairs)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"window_alibi_bf16: B={w.B} H={w.Hq} N={w.N} d={w.d} causal, window {window}, "
+                               f"ALiBi slopes 2^(-8h/H), fwd", "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d,
+                   "window": window, "alibi": True, "seed": SEED, "pass": "fwd"},
+        "roofline": {
+            "kernel": "attn_fwd_kernel<bf16, d=128, causal, window/ALiBi>",
+            "bound": "mfma",
+            "achieved": round(flops / (ms_call * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -222,6 +294,9 @@ def main():
               "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "window_alibi_bf16":
+        bench_window(args)
+        return
     if args.workload != WORKLOAD:
         bench_decode(args)
         return

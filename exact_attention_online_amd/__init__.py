@@ -12,11 +12,11 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
            "attn_status_string")
 
@@ -54,6 +54,8 @@ def load():
     lib.attn_bwd_dkdv.restype = i
     lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
+    lib.attn_fwd_ext.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, vp]
+    lib.attn_fwd_ext.restype = i
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i] * 7
     lib.attn_fwd_splitkv_workspace_size.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, sz, vp]
@@ -122,6 +124,30 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, dt, None, None, None, _stream(q.device)))
+    return out, lse
+
+
+def fwd_ext(q, k, v, causal: bool = False, scale: float | None = None, window: int = 0, alibi_slopes=None,
+            out=None, lse=None):
+    """attn_fwd with a sliding window (0 = none) and/or ALiBi slopes (float [Hq] device tensor)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise AttnError("q, k, v must share a dtype")
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    sl = None
+    if alibi_slopes is not None:
+        if (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq or not alibi_slopes.is_contiguous()
+                or alibi_slopes.device != q.device):
+            raise AttnError("alibi_slopes must be a contiguous float32 device tensor of Hq values")
+        sl = _ptr(alibi_slopes)
+    _check(load().attn_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                               int(bool(causal)), scale, dt, int(window), sl, _stream(q.device)))
     return out, lse
 
 

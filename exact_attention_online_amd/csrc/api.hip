@@ -20,6 +20,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                          int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
                          const void* workspace, hipStream_t stream);
+hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                          int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
+                          hipStream_t stream);
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
                            int d, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
@@ -88,6 +91,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                         (hipStream_t)stream);
   }
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                 int d, int causal, float softmax_scale, int dtype, int window, const float* alibi_slopes,
+                 attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale) || window < 0) return ATTN_ERR_INVALID;
+  if (alibi_slopes != nullptr && ((uintptr_t)alibi_slopes & 3u) != 0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  const int st = check_sizes(B, Hq, Hkv, N, d);
+  if (st != ATTN_OK) return st;
+  return eao::launch_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_scale, dtype == ATTN_BF16,
+                             window, alibi_slopes, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {

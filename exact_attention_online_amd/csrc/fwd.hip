@@ -51,11 +51,18 @@ struct FwdTile {
 };
 
 
-template <bool BF16, int D, int QB, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+// EXT adds the local (sliding-window) mask and the ALiBi bias ("FlashAttention-2: Faster Attention
+// with Better Parallelism and Work Partitioning", OpenReview discussion, author responses: FA2
+// supports ALiBi and local, i.e. sliding-window, attention): with window > 0, key j is visible to
+// query i only if i - j < window (and, without the causal mask, j - i < window); with slopes,
+// score (i, j) of head h gets - slopes[h] * |i - j| added after the softmax scale.  Every tile
+// of an EXT launch takes the masked path; tiles wholly before the window start of the
+// workgroup's first row are not visited.
+template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false>
+__global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int BH, int nqb,
-    float c /* softmax_scale * log2(e) */) {
+    float c /* softmax_scale * log2(e) */, int window, const float* __restrict__ slopes, float inv_scale) {
   using T = FwdTile<D, BC>;
   constexpr int CH = T::CH, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int BR = 4 * QB * 32;
@@ -66,10 +73,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) short k_lds1[T::ELEMS];
   __shared__ __attribute__((aligned(1024))) short v_lds0[T::ELEMS];
   __shared__ __attribute__((aligned(1024))) short v_lds1[T::ELEMS];
-  auto Ks = [&](auto par) -> short* {
+  auto Ks = [&](auto par) -> short* __attribute__((always_inline)) {
     if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
   };
-  auto Vs = [&](auto par) -> short* {
+  auto Vs = [&](auto par) -> short* __attribute__((always_inline)) {
     if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
   };
 
@@ -114,8 +121,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x16_t{};
   }
 
-  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const bool win = EXT && window > 0;
+  const int kend = CAUSAL ? min(N, q0 + BR) : (win ? min(N, q0 + BR - 1 + window) : N);
   const int ntiles = (kend + BC - 1) / BC;
+  // first tile with a key inside the window of the workgroup's first row
+  const int jfirst = win ? max(0, q0 - window + 1) / BC : 0;
+  // ALiBi in units of the raw scores (the softmax scale multiplies later): -slope / scale
+  const float ab = (EXT && slopes != nullptr) ? -slopes[h] * inv_scale : 0.f;
 
   // K/V of this head through bounds-checked buffer loads: keys >= N read as zeros
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, (uint32_t)N * D * 2);
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int row = p / CH, pch = p % CH;
     goff[i] = ((uint32_t)row * D + ((pch ^ swz<D>(row)) << 3)) * 2;
   }
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, short* dst, int kt0) {
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, short* dst, int kt0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::PIECES / 4; ++i)
       buffer_load16_lds(rs, dst + 512 * (4 * i + w), goff[i] + (uint32_t)kt0 * D * 2);
@@ -149,10 +161,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 
   // a wave takes part in tiles [0, jact): under causal masking, tiles whose first key lies after
   // the wave's last query row are skipped (the wave still helps stage them)
-  const int jact = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, qw_last / BC + 1) : ntiles);
+  const int jact = (qw >= N) ? 0
+                   : (CAUSAL ? min(ntiles, qw_last / BC + 1)
+                             : (win ? min(ntiles, (qw_last + window - 1) / BC + 1) : ntiles));
 
   // S^T = K Q^T for the key tile in K buffer `par`
-  auto compute_s = [&](auto par, f32x16_t (&s)[QB][KB]) {
+  auto compute_s = [&](auto par, f32x16_t (&s)[QB][KB]) __attribute__((always_inline)) {
     const short* Kb = Ks(par);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -172,13 +186,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // staging of one iteration: K_{j+2} replaces K_j (read while computing S^T of tile j, one
   // iteration ago), V_{j+1} replaces V_{j-1} (read one iteration ago)
   // (tile j lives in K and V buffers j % 2 = par)
-  auto stage = [&](int j, auto par) {
+  auto stage = [&](int j, auto par) __attribute__((always_inline)) {
     using Other = std::integral_constant<int, 1 - decltype(par)::value>;
     if (j + 2 < ntiles) load_tile(krs, Ks(par), (j + 2) * BC);
     if (j + 1 < ntiles) load_tile(vrs, Vs(Other{}), (j + 1) * BC);
   };
   // the loads of this iteration have landed in LDS and every wave is done with this tile
-  auto publish = [&]() {
+  auto publish = [&]() __attribute__((always_inline)) {
     wait_all_loads();
     __syncthreads();
   };
@@ -189,8 +203,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // scheduler overlaps matrix and vector work.  MASK selects the variant with causal / key-tail
   // masking.
   f32x16_t sA[QB][KB], sB[QB][KB];   // S^T of even / odd tiles
-  auto body = [&](int j, auto par, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // MODE 0: no mask; 1: masked (causal diagonal, key tail, window edges; ALiBi under EXT);
+  // 2: no mask, ALiBi bias only (EXT tiles inside the band)
+  auto body = [&](int j, auto par, auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool MASK = MODE == 1;
     constexpr int P = decltype(par)::value;
     using Other = std::integral_constant<int, 1 - P>;
     auto& sc = P == 0 ? sA : sB;
@@ -201,7 +218,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     float muse[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if constexpr (MASK) {
+      if constexpr (EXT && MODE != 0) {
+        // distance qrow - key of register r as an exact float: (qrow - kt0 - 4g) - constant
+        const int qrow = qw + 32 * qb + l32;
+        const float dq = (float)(qrow - kt0 - 4 * g);
+        const float lo = (float)(qrow - N);                 // key >= N  <=>  qrow - key <= lo
+        const float wf = win ? (float)window : INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float diff = dq - (float)(32 * kb + 8 * (r >> 2) + (r & 3));
+            const float biased = __builtin_fmaf(__builtin_fabsf(diff), ab, sc[qb][kb][r]);
+            if constexpr (MASK) {
+              const bool vis = diff > lo && diff < wf && (CAUSAL ? diff >= 0.f : diff > -wf);
+              sc[qb][kb][r] = vis ? biased : -INFINITY;
+            } else {
+              sc[qb][kb][r] = biased;
+            }
+          }
+      } else if constexpr (MASK) {
         const int qrow = qw + 32 * qb + l32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -274,36 +310,75 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     publish();
   };
   // staging only, for tiles this wave skips
-  auto idle = [&](int j) {
+  auto idle = [&](int j) __attribute__((always_inline)) {
     if (j & 1) stage(j, Par1{});
     else stage(j, Par0{});
     publish();
   };
 
-  // prologue: K_0, V_0, K_1 staged; S^T of tile 0
-  load_tile(krs, Ks(Par0{}), 0);
-  load_tile(vrs, Vs(Par0{}), 0);
-  if (ntiles > 1) load_tile(krs, Ks(Par1{}), BC);
-  publish();
-  if (jact > 0) compute_s(Par0{}, sA);
-  // the first iteration overwrites K buffer 0
+  // prologue: K and V of tile jfirst, K of tile jfirst + 1 staged; S^T of tile jfirst (tile j
+  // lives in the buffers of parity j % 2; jfirst is 0 unless a window skips leading tiles)
+  auto prologue = [&](auto par) __attribute__((always_inline)) {
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    load_tile(krs, Ks(par), jfirst * BC);
+    load_tile(vrs, Vs(par), jfirst * BC);
+    if (jfirst + 1 < ntiles) load_tile(krs, Ks(Other{}), (jfirst + 1) * BC);
+    publish();
+    if (jact > jfirst) compute_s(par, decltype(par)::value == 0 ? sA : sB);
+  };
+  if (jfirst & 1) prologue(Par1{});
+  else prologue(Par0{});
+  // the first iteration overwrites the K buffer of tile jfirst
   __syncthreads();
 
-  // tiles [0, jmask) need no masking for any wave of the workgroup
-  const int jmask = min(jact, CAUSAL ? min(q0, N) / BC : N / BC);
-  int j = 0;
-  for (; j + 2 <= jmask; j += 2) {
-    body(j, Par0{}, std::false_type{});
-    body(j + 1, Par1{}, std::false_type{});
+  // tiles [jlo, jmask) need no masking for any wave of the workgroup: below the causal diagonal
+  // (keys < q0), before the key tail, and (window) inside the band of every row of the block;
+  // tiles [jfirst, jlo) and [jmask, jact) are masked
+  using Mode0 = std::integral_constant<int, 0>;
+  using Mode1 = std::integral_constant<int, 1>;
+  using Mode2 = std::integral_constant<int, 2>;
+  int jmask = min(jact, CAUSAL ? min(q0, N) / BC : N / BC);
+  int jlo = jfirst;
+  if (win) {
+    jlo = max(jfirst, (max(0, q0 + BR - window) + BC - 1) / BC);
+    if (!CAUSAL) jmask = min(jmask, (q0 + window) / BC);
   }
-  if (j < jmask) {
-    body(j, Par0{}, std::false_type{});
-    ++j;
+  jmask = max(jmask, jlo);
+  int j = jfirst;
+  auto run_masked = [&](int end) __attribute__((always_inline)) {
+    for (; j < end; ++j) {
+      if (j & 1) body(j, Par1{}, Mode1{});
+      else body(j, Par0{}, Mode1{});
+    }
+  };
+  if constexpr (EXT) {
+    // one loop (a single register assignment for the running state), the tile's kind and buffer
+    // parity chosen per iteration
+    const bool alibi = ab != 0.f;
+    for (; j < jact; ++j) {
+      const bool inner = j >= jlo && j < jmask;
+      if (j & 1) {
+        if (!inner) body(j, Par1{}, Mode1{});
+        else if (alibi) body(j, Par1{}, Mode2{});
+        else body(j, Par1{}, Mode0{});
+      } else {
+        if (!inner) body(j, Par0{}, Mode1{});
+        else if (alibi) body(j, Par0{}, Mode2{});
+        else body(j, Par0{}, Mode0{});
+      }
+    }
+  } else {
+    // jfirst = jlo = 0: tiles [0, jmask) in pairs of parities 0, 1
+    for (; j + 2 <= jmask; j += 2) {
+      body(j, Par0{}, Mode0{});
+      body(j + 1, Par1{}, Mode0{});
+    }
+    if (j < jmask) {
+      body(j, Par0{}, Mode0{});
+      ++j;
+    }
   }
-  for (; j < jact; ++j) {
-    if (j & 1) body(j, Par1{}, std::true_type{});
-    else body(j, Par0{}, std::true_type{});
-  }
+  run_masked(jact);
   for (; j < ntiles; ++j) idle(j);
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
@@ -337,8 +412,36 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
   const int BH = B * Hq;
   auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL>;
   hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e);
+                     (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e, 0,
+                     (const float*)nullptr, 1.f);
   return hipGetLastError();
+}
+
+template <bool BF16, int D, bool CAUSAL>
+static hipError_t launch_fwd_ext_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                   int Hkv, int N, float scale, int window, const float* slopes, hipStream_t stream) {
+  constexpr int BR = 128;
+  const int nqb = (N + BR - 1) / BR;
+  const int BH = B * Hq;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, 1, 64, CAUSAL, true>), dim3(nqb * BH), dim3(256), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH,
+                     nqb, scale * kLog2e, window, slopes, 1.f / scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                          int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
+                          hipStream_t stream) {
+#define EAO_FWDX(BF, DD, CA) \
+  return launch_fwd_ext_t<BF, DD, CA>(q, k, v, o, lse, B, Hq, Hkv, N, scale, window, slopes, stream)
+  if (bf16) {
+    if (d == 128) { if (causal) EAO_FWDX(true, 128, true); else EAO_FWDX(true, 128, false); }
+    else { if (causal) EAO_FWDX(true, 64, true); else EAO_FWDX(true, 64, false); }
+  } else {
+    if (d == 128) { if (causal) EAO_FWDX(false, 128, true); else EAO_FWDX(false, 128, false); }
+    else { if (causal) EAO_FWDX(false, 64, true); else EAO_FWDX(false, 64, false); }
+  }
+#undef EAO_FWDX
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,

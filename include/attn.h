@@ -71,6 +71,19 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const float* q_descale, const float* k_descale, const float* v_descale,
              attn_stream_t stream);
 
+/* Forward with a local (sliding-window) mask and/or an ALiBi bias ("FlashAttention-2: Faster
+ * Attention with Better Parallelism and Work Partitioning", OpenReview discussion, author
+ * responses: FA2 supports ALiBi, and local, i.e. sliding-window, attention).  Arguments as for
+ * attn_fwd (dtype ATTN_F16 or ATTN_BF16), plus:
+ *   window: 0 = no window; otherwise key j is visible to query i only if i - j < window, and,
+ *     when causal is 0, also j - i < window (with causal, j <= i as well).
+ *   alibi_slopes: NULL, or device float [Hq] (4-byte aligned): score (i, j) of query head h is
+ *     softmax_scale * q_i . k_j - alibi_slopes[h] * |i - j|.
+ * With window 0 and no slopes the result equals attn_fwd's.  Returns an attn_status_t. */
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+                 int window, const float* alibi_slopes, attn_stream_t stream);
+
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
  * up to a multiple of 64: D = rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
  * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and

@@ -119,3 +119,12 @@ def test_splitkv_workspace_size():
     # splits are clamped to the number of 128-key tiles and never empty
     assert ws(1, 8, 2, 1, 300, 128, 64) == ws(1, 8, 2, 1, 300, 128, 3)
     assert ws(1, 8, 1, 5, 100, 128, 0) == 0     # 8 heads x 5 rows do not fit one 32-row tile
+
+
+def test_fwd_ext_rejects_bad_arguments():
+    lib = eao.load()
+    ok = (P, P, P, P, P, 1, 2, 2, 100, 128, 1, 0.1, 1)
+    assert lib.attn_fwd_ext(*ok, -1, NULL, NULL) == 1                       # negative window
+    assert lib.attn_fwd_ext(*ok, 4, ctypes.c_void_p(0x7F0000001002), NULL) == 1   # misaligned slopes
+    assert lib.attn_fwd_ext(P, P, P, P, P, 1, 2, 2, 100, 128, 1, 0.1, 2, 4, NULL, NULL) == 2   # fp8
+    assert lib.attn_fwd_ext(P, P, P, P, P, 1, 2, 2, 100, 96, 1, 0.1, 1, 4, NULL, NULL) == 2    # head dim
