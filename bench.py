@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16"],
+                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8"],
                     help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
                          "shape's forward with a 4096-key sliding window and ALiBi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -286,6 +286,88 @@ def bench_window(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_fp8(args):
+    """FP8 forward (B=4, H=16, N=4096, d=128, non-causal, e4m3 with per-128-row scales): TFLOP/s of
+    attn_fwd on prepared codes, against the dense fp8 MFMA peak; the preparation (Hadamard +
+    quantisation, HBM-bound) is timed separately and not counted."""
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import WORKLOADS, draw_fp8
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    w = WORKLOADS["fp8"]
+    dev = torch.device("cuda:0")
+    q, k, v, signs = draw_fp8(w.B, w.Hq, w.N, w.d, SEED)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    ts = torch.from_numpy(signs).to(dev)
+
+    def prep():
+        return (eao.fp8_prep(tq, ts), eao.fp8_prep(tk, ts), eao.fp8_prep(tv, None))
+
+    (q8, qs), (k8, ks), (v8, vs) = prep()
+    o = torch.empty(w.B, w.Hq, w.N, w.d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.Hq, w.N, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        eao.fwd_fp8(q8, k8, v8, qs, ks, vs, w.causal, w.scale, o, lse)
+        prep()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        eao.fwd_fp8(q8, k8, v8, qs, ks, vs, w.causal, w.scale, o, lse)
+        evs[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][2].record()
+        prep()
+        evs[i][3].record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_prep = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    if not torch.isfinite(o.float()).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+    f_fwd = 4.0 * w.B * w.Hq * w.N * w.N * w.d / (2 if w.causal else 1)
+    prep_bytes = 3 * w.B * w.Hq * w.N * w.d * (4 + 1) + 3 * w.B * w.Hq * (w.N // 128) * 4
+    out = {
+        "metric": "fp8 attention fwd TFLOPs/s (e4m3, block scales + Hadamard)",
+        "value": round(f_fwd / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"fp8: B={w.B} H={w.Hq} N={w.N} d={w.d} non-causal, 0.1% outliers x10, e4m3 per "
+                               f"128 rows, Hadamard on Q and K", "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": SEED, "pass": "fwd"},
+        "prep_ms": round(ms_prep, 4),
+        "prep_gbps": round(prep_bytes / (ms_prep * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "fwd_fp8_kernel<non-causal>",
+            "bound": "mfma",
+            "achieved": round(f_fwd / (ms_call * 1e-3) / 1e12, 2),
+            "peak": 5033.2,
+            "unit": "TFLOP/s",
+            "frac": round(f_fwd / (ms_call * 1e-3) / 1e12 / 5033.2, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -294,6 +376,9 @@ def main():
               "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "fp8":
+        bench_fp8(args)
+        return
     if args.workload == "window_alibi_bf16":
         bench_window(args)
         return

@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "E4M3_MAX", "QBLOCK", "sylvester", "fwht_f32", "incoherent_f32", "e4m3_decode", "e4m3_encode",
-    "block_quantize", "dequantize",
+    "block_quantize", "tensor_quantize", "dequantize",
 ]
 
 E4M3_MAX = 448.0
@@ -126,6 +126,19 @@ def block_quantize(x: np.ndarray, block: int = QBLOCK):
         y = (blk / sc[:, :, None, None]).astype(np.float32)     # float32 division, correctly rounded
         codes[:, :, i * block:(i + 1) * block, :] = e4m3_encode(y)
         scales[:, :, i] = sc
+    return codes, scales
+
+
+def tensor_quantize(x: np.ndarray, block: int = QBLOCK):
+    """The per-tensor scaling that the FlashAttention-3 abstract contrasts with block quantisation:
+    one scale amax / 448 for the whole tensor (all heads, all rows), returned in the block layout
+    (every entry equal) so that the same fp8 kernel consumes it."""
+    x = np.asarray(x, dtype=np.float32)
+    B, H, N, d = x.shape
+    amax = np.float32(np.abs(x).max())
+    sc = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    codes = e4m3_encode((x / sc).astype(np.float32))
+    scales = np.full((B, H, -(-N // block)), sc, dtype=np.float32)
     return codes, scales
 
 

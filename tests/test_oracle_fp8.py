@@ -102,3 +102,21 @@ def test_block_quantize_properties():
     # relative error of a normal e4m3 value is at most 2^-4; subnormals add an absolute 2^-10 * scale
     bound = np.abs(x) * 2.0 ** -4 + np.repeat(scales, 128, axis=2)[:, :, :300, None] * 2.0 ** -10
     assert np.all(np.abs(deq - x) <= bound + 1e-12)
+
+
+def test_tensor_quantize_properties():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 3, 300, 16)).astype(np.float32)
+    x[1, 2, 17, 5] = -9.0                              # the tensor's amax lands on code -448
+    codes, scales = fp8.tensor_quantize(x)
+    assert scales.shape == (2, 3, 3) and np.all(scales == np.float32(9.0 / np.float32(448.0)))
+    assert codes[1, 2, 17, 5] == 0xFE
+    # one block covering the whole tensor is the same quantiser as block_quantize
+    one = x[:1, :1, :128]
+    c1, s1 = fp8.tensor_quantize(one)
+    c2, s2 = fp8.block_quantize(one)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    deq = fp8.dequantize(codes, scales)
+    bound = np.abs(x) * 2.0 ** -4 + float(scales[0, 0, 0]) * 2.0 ** -10
+    assert np.all(np.abs(deq - x) <= bound + 1e-12)
+    assert np.all(fp8.tensor_quantize(np.zeros((1, 1, 5, 4), np.float32))[1] == 1.0)
