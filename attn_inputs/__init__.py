@@ -11,6 +11,9 @@ Recipe (applies to every workload):
   * rounding to fp16/bf16 is round-to-nearest-even through torch's dtype conversion;
   * decoding shapes (few query rows against a long key sequence): Q [B,Hq,Nq,d] then K, V
     [B,Hkv,Nk,d], same generator and order;
+  * packed variable-length batches: the sequence lengths first (``varlen_lengths``: integers
+    uniform in [lo, hi] from their own generator), then Q [Hq,T,d], K, V [Hkv,T,d] with T the sum
+    of the lengths, same order as above;
   * fp8 extras (drawn after dO would be, from the same generator): for each of Q, K, V in that
     order, ``round(0.001 * numel)`` distinct flat indices chosen uniformly without replacement,
     whose entries are multiplied by 10 (outliers); then one sign vector of length d with entries
@@ -23,7 +26,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "DECODE_WORKLOADS", "DecodeWorkload", "draw", "draw_decode", "draw_fp8",
-           "round_to", "DTYPES"]
+           "draw_varlen", "varlen_lengths", "round_to", "DTYPES"]
 
 DTYPES = ("fp16", "bf16")
 
@@ -97,6 +100,26 @@ def draw_decode(B, Hq, Hkv, Nq, Nk, d, seed):
     k = gen.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     v = gen.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     return q, k, v
+
+
+def varlen_lengths(count, lo, hi, seed):
+    """`count` sequence lengths, integers uniform in [lo, hi] (PCG64(seed))."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    return gen.integers(lo, hi + 1, size=count).astype(np.int64)
+
+
+def draw_varlen(lengths, Hq, Hkv, d, seed):
+    """Packed float32 Q [Hq,T,d], K, V [Hkv,T,d] (T = sum of lengths) and the int32 offsets
+    cu_seqlens [len(lengths) + 1]."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    gen = np.random.Generator(np.random.PCG64(seed))
+    q = gen.standard_normal((Hq, T, d), dtype=np.float32)
+    k = gen.standard_normal((Hkv, T, d), dtype=np.float32)
+    v = gen.standard_normal((Hkv, T, d), dtype=np.float32)
+    return q, k, v, cu
 
 
 def round_to(x: np.ndarray, dtype: str):

@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8"],
+                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8", "varlen_bf16"],
                     help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
                          "shape's forward with a 4096-key sliding window and ALiBi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,6 +368,75 @@ def bench_fp8(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_varlen(args):
+    """Forward over 16 causal sequences packed without padding, lengths uniform in [128, 8192]
+    (seed 3), H=16, d=128, bf16: TFLOP/s with 4 d flops per query-key pair, halved for causal."""
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import draw_varlen, round_to, varlen_lengths
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    H, d = 16, 128
+    lens = varlen_lengths(16, 128, 8192, seed=SEED)
+    q32, k32, v32, cu = draw_varlen(lens, H, H, d, SEED)
+    dev = torch.device("cuda:0")
+    q, k, v = (round_to(x, "bf16").to(dev).contiguous() for x in (q32, k32, v32))
+    del q32, k32, v32
+    tcu = torch.from_numpy(cu).to(dev)
+    T, ms_len = int(cu[-1]), int(lens.max())
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        eao.fwd_varlen(q, k, v, tcu, ms_len, True, None, o, lse)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        eao.fwd_varlen(q, k, v, tcu, ms_len, True, None, o, lse)
+        evs[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    if not torch.isfinite(o).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+    flops = 4.0 * H * d * float((lens.astype(float) ** 2).sum()) / 2
+    out = {
+        "metric": "attention fwd TFLOPs/s over packed variable-length causal sequences",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"varlen_bf16: 16 sequences, lengths uniform in [128, 8192] (T={T}, longest {ms_len}), "
+                               f"H={H} d={d} causal fwd", "H": H, "d": d, "T": T, "lengths": lens.tolist(),
+                   "seed": SEED, "pass": "fwd"},
+        "roofline": {
+            "kernel": "attn_fwd_kernel<bf16, d=128, causal, varlen>",
+            "bound": "mfma",
+            "achieved": round(flops / (ms_call * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -376,6 +445,9 @@ def main():
               "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "varlen_bf16":
+        bench_varlen(args)
+        return
     if args.workload == "fp8":
         bench_fp8(args)
         return

@@ -12,11 +12,11 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "fwd_varlen", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
            "attn_status_string")
 
@@ -55,6 +55,8 @@ def load():
     lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
     lib.attn_fwd_ext.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, vp]
+    lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 7 + [f, i, vp]
+    lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_ext.restype = i
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i] * 7
     lib.attn_fwd_splitkv_workspace_size.restype = sz
@@ -148,6 +150,34 @@ def fwd_ext(q, k, v, causal: bool = False, scale: float | None = None, window: i
         sl = _ptr(alibi_slopes)
     _check(load().attn_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
                                int(bool(causal)), scale, dt, int(window), sl, _stream(q.device)))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None, out=None,
+               lse=None):
+    """O [Hq,T,d], LSE [Hq,T] for sequences packed along T (q [Hq,T,d], k/v [Hkv,T,d]); cu_seqlens is a
+    device int32 tensor [B+1] of sequence offsets."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise AttnError(f"expected q [Hq,T,d], k/v [Hkv,T,d]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    if k.shape[1] != T or k.shape[2] != d:
+        raise AttnError("q and k/v disagree in T or d")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise AttnError("q, k, v must be contiguous device tensors of one dtype on one device")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise AttnError("cu_seqlens must be an int32 device tensor [B+1]")
+    B = cu_seqlens.numel() - 1
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens.contiguous()), B,
+                                  Hq, Hkv, T, int(max_seqlen), d, int(bool(causal)), scale, dt, _stream(q.device)))
     return out, lse
 
 

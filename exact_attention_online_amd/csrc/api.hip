@@ -23,6 +23,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                           int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
                           hipStream_t stream);
+hipError_t launch_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                             int B, int Hq, int Hkv, int T, int max_seqlen, int d, bool causal, float scale,
+                             bool bf16, hipStream_t stream);
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
                            int d, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
@@ -104,6 +107,22 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
   if (st != ATTN_OK) return st;
   return eao::launch_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_scale, dtype == ATTN_BF16,
                              window, alibi_slopes, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+                    int Hq, int Hkv, int T, int max_seqlen, int d, int causal, float softmax_scale, int dtype,
+                    attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID;
+  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u) != 0) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale) || max_seqlen < 1 || max_seqlen > T) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  // the packed tensors are one batch of T rows per head
+  int st = check_sizes(1, Hq, Hkv, T, d);
+  if (st != ATTN_OK) return st;
+  if (B < 1 || (double)B * Hq * ((max_seqlen + 127) / 128) > 2.0e9) return ATTN_ERR_INVALID;
+  return eao::launch_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, T, max_seqlen, d, causal != 0,
+                                softmax_scale, dtype == ATTN_BF16, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 

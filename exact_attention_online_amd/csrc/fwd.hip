@@ -58,11 +58,19 @@ struct FwdTile {
 // score (i, j) of head h gets - slopes[h] * |i - j| added after the softmax scale.  Every tile
 // of an EXT launch takes the masked path; tiles wholly before the window start of the
 // workgroup's first row are not visited.
-template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false>
+//
+// VARLEN: sequences of different lengths packed without padding ("FlashAttention-2: Faster
+// Attention with Better Parallelism and Work Partitioning", OpenReview discussion, author
+// responses: variable sequence lengths, concatenated with an array of lengths).  Q, K, V, O are
+// [H, T, d] and LSE [H, T] with T = N_in packed tokens; sequence b is rows cu_seqlens[b] ..
+// cu_seqlens[b + 1] - 1 of every head (clamped to [0, T]) and attends only within itself.  The
+// grid covers the longest sequence (nqb blocks of BR rows); blocks past a sequence's end exit.
+template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false, bool VARLEN = false>
 __global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int BH, int nqb,
-    float c /* softmax_scale * log2(e) */, int window, const float* __restrict__ slopes, float inv_scale) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N_in, int BH, int nqb,
+    float c /* softmax_scale * log2(e) */, int window, const float* __restrict__ slopes, float inv_scale,
+    const int* __restrict__ cu_seqlens) {
   using T = FwdTile<D, BC>;
   constexpr int CH = T::CH, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int BR = 4 * QB * 32;
@@ -88,8 +96,21 @@ __global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
   const int bh = L % BH;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
-  const size_t q_off = ((size_t)b * Hq + h) * (size_t)N * D;
-  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
+  int N = N_in;
+  size_t q_off, kv_off, lse_off;
+  if constexpr (VARLEN) {
+    const int s0 = min(max(cu_seqlens[b], 0), N_in);
+    const int s1 = min(max(cu_seqlens[b + 1], s0), N_in);
+    N = s1 - s0;
+    if (qblk * BR >= N) return;               // the whole workgroup: no barrier has been reached
+    q_off = ((size_t)h * N_in + s0) * D;
+    kv_off = ((size_t)kvh * N_in + s0) * D;
+    lse_off = (size_t)h * N_in + s0;
+  } else {
+    q_off = ((size_t)b * Hq + h) * (size_t)N * D;
+    kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
+    lse_off = (size_t)bh * N;
+  }
   const uint16_t* Qp = Q + q_off;
 
   const int q0 = qblk * BR;
@@ -399,7 +420,7 @@ __global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
           pk.y = pack2<BF16>(o[qb][db][4 * rr + 2] * inv, o[qb][db][4 * rr + 3] * inv);
           *(uint2*)(Op + d0) = pk;
         }
-      if (g == 0) LSE[(size_t)bh * N + qrow] = (m[qb] + __log2f(lt)) * kLn2;
+      if (g == 0) LSE[lse_off + qrow] = (m[qb] + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -413,7 +434,7 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
   auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL>;
   hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e, 0,
-                     (const float*)nullptr, 1.f);
+                     (const float*)nullptr, 1.f, (const int*)nullptr);
   return hipGetLastError();
 }
 
@@ -425,7 +446,7 @@ static hipError_t launch_fwd_ext_t(const void* q, const void* k, const void* v, 
   const int BH = B * Hq;
   hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, 1, 64, CAUSAL, true>), dim3(nqb * BH), dim3(256), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH,
-                     nqb, scale * kLog2e, window, slopes, 1.f / scale);
+                     nqb, scale * kLog2e, window, slopes, 1.f / scale, (const int*)nullptr);
   return hipGetLastError();
 }
 
@@ -442,6 +463,34 @@ hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, 
     else { if (causal) EAO_FWDX(false, 64, true); else EAO_FWDX(false, 64, false); }
   }
 #undef EAO_FWDX
+}
+
+template <bool BF16, int D, bool CAUSAL>
+static hipError_t launch_fwd_varlen_t(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      const int* cu_seqlens, int B, int Hq, int Hkv, int T, int max_seqlen,
+                                      float scale, hipStream_t stream) {
+  constexpr int BR = 128;
+  const int nqb = (max_seqlen + BR - 1) / BR;
+  const int BH = B * Hq;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, 1, 64, CAUSAL, false, true>), dim3(nqb * BH), dim3(256), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, T, BH,
+                     nqb, scale * kLog2e, 0, (const float*)nullptr, 1.f, cu_seqlens);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                             int B, int Hq, int Hkv, int T, int max_seqlen, int d, bool causal, float scale,
+                             bool bf16, hipStream_t stream) {
+#define EAO_FWDV(BF, DD, CA) \
+  return launch_fwd_varlen_t<BF, DD, CA>(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, T, max_seqlen, scale, stream)
+  if (bf16) {
+    if (d == 128) { if (causal) EAO_FWDV(true, 128, true); else EAO_FWDV(true, 128, false); }
+    else { if (causal) EAO_FWDV(true, 64, true); else EAO_FWDV(true, 64, false); }
+  } else {
+    if (d == 128) { if (causal) EAO_FWDV(false, 128, true); else EAO_FWDV(false, 128, false); }
+    else { if (causal) EAO_FWDV(false, 64, true); else EAO_FWDV(false, 64, false); }
+  }
+#undef EAO_FWDV
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,

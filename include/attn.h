@@ -84,6 +84,22 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
                  int window, const float* alibi_slopes, attn_stream_t stream);
 
+/* Forward over variable-length sequences packed without padding ("FlashAttention-2: Faster
+ * Attention with Better Parallelism and Work Partitioning", OpenReview discussion, author
+ * responses: sequences are concatenated with no padding token and an array gives the lengths).
+ *   q [Hq,T,d], k, v [Hkv,T,d], o [Hq,T,d] in `dtype` (ATTN_F16 / ATTN_BF16), lse [Hq,T] float:
+ *   the [B,H,N,d] layout of attn_fwd with the B sequences concatenated along the rows.
+ *   cu_seqlens: device int32 [B+1], 0 = cu_seqlens[0] <= ... <= cu_seqlens[B] = T; sequence b is
+ *   rows cu_seqlens[b] .. cu_seqlens[b+1]-1 and attends only within itself (causal: as in
+ *   attn_fwd, per sequence).  Entries are read on the device and clamped to [0, T], so malformed
+ *   offsets give wrong rows, never an access outside the tensors.
+ *   max_seqlen: at least the longest sequence (1 <= max_seqlen <= T); rows past max_seqlen of a
+ *   longer sequence are not computed.  Sequences of length 0 are allowed.
+ * Returns an attn_status_t. */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int B, int Hq, int Hkv, int T, int max_seqlen, int d,
+                    int causal, float softmax_scale, int dtype, attn_stream_t stream);
+
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
  * up to a multiple of 64: D = rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
  * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and

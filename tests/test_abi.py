@@ -128,3 +128,17 @@ def test_fwd_ext_rejects_bad_arguments():
     assert lib.attn_fwd_ext(*ok, 4, ctypes.c_void_p(0x7F0000001002), NULL) == 1   # misaligned slopes
     assert lib.attn_fwd_ext(P, P, P, P, P, 1, 2, 2, 100, 128, 1, 0.1, 2, 4, NULL, NULL) == 2   # fp8
     assert lib.attn_fwd_ext(P, P, P, P, P, 1, 2, 2, 100, 96, 1, 0.1, 1, 4, NULL, NULL) == 2    # head dim
+
+
+def test_fwd_varlen_rejects_bad_arguments():
+    lib = eao.load()
+    a = [P, P, P, P, P, P, 3, 4, 2, 1000, 500, 128, 1, 0.1, 1, NULL]
+    assert lib.attn_fwd_varlen(*a[:5], NULL, *a[6:]) == 1                    # no offsets
+    bad = list(a); bad[10] = 1001                                            # max_seqlen > T
+    assert lib.attn_fwd_varlen(*bad) == 1
+    bad = list(a); bad[10] = 0
+    assert lib.attn_fwd_varlen(*bad) == 1
+    bad = list(a); bad[11] = 96                                              # head dim
+    assert lib.attn_fwd_varlen(*bad) == 2
+    bad = list(a); bad[14] = 2                                               # fp8
+    assert lib.attn_fwd_varlen(*bad) == 2
