@@ -8,24 +8,24 @@
 //   dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three kernels on the caller's stream, none of them atomic:
-//   1. bwd_pre: per query row D = rowsum(dO * O) and LSE * log2(e), and the 64-row tiles of Q
-//      and dO written transposed ([d][64 rows], see the workspace layout below), all in the
+//   1. bwd_pre: per query row -D = -rowsum(dO * O) and LSE * log2(e), and the 64-row tiles of
+//      Q and dO written transposed ([d][64 rows], see the workspace layout below), all in the
 //      caller's workspace.
-//   2. bwd_dkdv: one workgroup per (batch, K/V head, block of 128 keys); each of the 4 waves
-//      owns 32 keys and keeps their K and V fragments and its dK^T, dV^T accumulators in
-//      registers for the whole kernel.  The workgroup walks every query head of the K/V head's
-//      group and every tile of 64 query rows (causal: from the diagonal on), so dK and dV are
-//      summed over the group in registers.  The tiles of Q, dO, Q^T and dO^T go straight from
-//      HBM into double-buffered LDS (direct buffer -> LDS loads, one tile ahead), LSE and D into
-//      registers.  Per tile, in two halves of 32 rows:
-//        S = Q K^T, dP = dO V^T   (A = Q / dO rows via ds_read_b128, B = K / V registers; a lane
-//                                  owns one key column of the accumulator)
-//        P = exp2(S * scale * log2e - LSE * log2e) (causal mask on the diagonal tiles only);
-//        dS = P * (dP - D);  dV^T += dO^T P, dK^T += Q^T dS with P and dS taken straight from
-//        the accumulators and dO^T, Q^T read as rows of the transposed tiles (ds_read_b128).
-//      Every LDS read is a 16-byte row read: the transposed copies cost one extra pass over Q
-//      and dO in the preprocess but halve the LDS instructions of the two transposed operands,
-//      and LDS instruction issue is what limits this kernel.
+//   2. bwd_dkdv: one workgroup of 8 waves per (batch, K/V head, block of 128 keys), in two
+//      roles over the same four quarters of 32 keys (one wave of each role per SIMD).  A "P
+//      wave" keeps its keys' K fragments and dV^T in registers, a "dS wave" their V fragments
+//      and dK^T.  The workgroup walks every query head of the K/V head's group and every tile
+//      of 64 query rows (causal: from the diagonal on), so dK and dV are summed over the group
+//      in registers.  The tiles of Q, dO, Q^T and dO^T and the rows' LSE2 and -D go straight
+//      from HBM into double-buffered LDS (direct buffer -> LDS loads, one tile ahead).  Per
+//      tile (a lane owns one key column of every accumulator):
+//        P wave:  S = Q K^T;  P = exp2(S * scale * log2e - LSE * log2e) (causal mask on the
+//                 diagonal tiles only), rounded to the input type and passed to the partner
+//                 through LDS;  dV^T += dO^T P
+//        dS wave: dP - D = dO V^T accumulated from -D;  dS = P (dP - D);  dK^T += Q^T dS
+//      with Q, dO read as rows of the row-major tiles and dO^T, Q^T as rows of the transposed
+//      tiles (all ds_read_b128).  Two contractions per wave keep each wave under 256
+//      registers, so two waves share a SIMD and one's vector work overlaps the other's MFMAs.
 //   3. bwd_dq: one workgroup per (batch, query head, block of 128 query rows), shaped like the
 //      forward: a lane owns one query row, so LSE and D are one register each.  Per key tile:
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T,
@@ -51,7 +51,7 @@ constexpr int kDqKeys = 64;     // keys per dQ step
 
 // Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256),
 // T = B * Hq * Npad * d * 2:
-//   [0, A)           D     float  [B*Hq][Npad]   rowsum(dO * O); 0 past N
+//   [0, A)           -D    float  [B*Hq][Npad]   -rowsum(dO * O); 0 past N
 //   [A, 2A)          LSE2  float  [B*Hq][Npad]   LSE * log2(e); +inf past N
 //   [2A, 2A + T)     Q^T   16-bit [B*Hq][Npad/64][d][64]
 //   [2A + T, 2A+2T)  dO^T  16-bit [B*Hq][Npad/64][d][64]
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
     if (ch == 0) {
       const size_t r = (size_t)bh * npad + q;
-      Dsum[r] = q < N ? acc : 0.f;
+      Dsum[r] = q < N ? -acc : 0.f;
       Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
     }
     *(uint4*)(tq + row * STR + 8 * ch) = qv;
@@ -178,35 +178,56 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ 2. dK, dV
-// Per step (one 64-row query tile): four tiles in LDS, double-buffered, each a distinct LDS
-// object so that direct loads into one buffer never make the compiler wait before reads of the
-// other: [Q | dO] ([64 rows][D], chunks XOR-swizzled by swz) and [Q^T | dO^T] ([D rows][64],
-// chunk c of row r at c ^ ((r / 2) % 8)).  Every operand is read with ds_read_b128; the tiles
-// are filled by direct buffer -> LDS loads (no staging registers, no LDS write instructions).
+// One workgroup of 8 waves per (batch, K/V head, block of 128 keys).  The waves come in two
+// roles over the same four quarters of 32 keys, one wave of each role per SIMD:
+//   P waves (0-3):  hold K and dV^T of their 32 keys; per query tile S = Q K^T, P = exp2(S c -
+//                   LSE2) (causal mask on the diagonal tiles), P rounded to the input type and
+//                   handed to the partner wave through LDS, then dV^T += dO^T P;
+//   dS waves (4-7): hold V and dK^T; dP - D = dO V^T accumulated from -D, then, with the
+//                   partner's P, dS = P (dP - D) and dK^T += Q^T dS.
+// Each wave does two of the four contractions and needs fewer than 256 registers, so two
+// waves share each SIMD and one wave's vector work runs beside the other's MFMAs.  Per step
+// (one 64-row query tile) the tiles [Q | dO] ([64 rows][D], chunks XOR-swizzled by swz) and
+// [Q^T | dO^T] ([D rows][64], chunk c of row r at c ^ ((r / 2) % 8)), and LSE2 and -D of the
+// 64 rows, go straight from HBM into double-buffered LDS (direct buffer -> LDS loads one step
+// ahead, each buffer a distinct LDS object); every operand read is a 16-byte row read.
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int npad, int nkb, float c /* scale * log2(e) */,
     float scale) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
-  constexpr int TILE = kBwdRows * D;                // 16-bit elements per tile
-  constexpr int PIECES = TILE * 2 / 1024;           // 1 KB direct-load pieces per tile
-  static_assert(PIECES % 4 == 0, "each wave moves the same number of pieces");
+  constexpr int NW = 8;                              // waves per workgroup
+  constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
+  constexpr int PIECES = TILE * 2 / 1024;            // 1 KB direct-load pieces per tile
+  static_assert(PIECES % NW == 0, "each wave moves the same number of pieces of every tile");
+  constexpr int PW = PIECES / NW;
   __shared__ __attribute__((aligned(1024))) short qd0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short qd1[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short tt0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short tt1[2 * TILE];
+  // [LSE2 of the 64 rows | zeros][-D of the 64 rows | zeros], 1 KB each
+  __shared__ __attribute__((aligned(1024))) float st0[512];
+  __shared__ __attribute__((aligned(1024))) float st1[512];
+  // P of each key quarter: [quarter][slot 2 * half + t][lane], 16 bytes each
+  __shared__ __attribute__((aligned(1024))) uint4 pex[4 * 4 * 64];
   auto QD = [&](auto par) -> short* __attribute__((always_inline)) {
     if constexpr (decltype(par)::value == 0) return qd0; else return qd1;
   };
   auto TT = [&](auto par) -> short* __attribute__((always_inline)) {
     if constexpr (decltype(par)::value == 0) return tt0; else return tt1;
   };
+  auto ST = [&](auto par) -> float* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return st0; else return st1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);            // the same, known to be uniform
+  const int role = wu >> 2;                                      // 0: P wave, 1: dS wave
+  const int kq = w & 3;                                         // key quarter
   const int G = Hq / Hkv;
   // key block major: under causal masking the first key blocks see the most query rows, so
   // the heaviest workgroups of every head start first
@@ -216,27 +237,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int bkv = L % BHkv;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int k0 = kblk * kBwdKeys;
-  const int kw = k0 + 32 * w;                       // this wave's first key
+  const int kw = k0 + 32 * kq;                      // this wave's first key
   const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
 
-  // persistent B operands of S = Q K^T and dP = dO V^T: this wave's 32 K and V rows
-  i16x8_t kf[KK], vf[KK];
+  // persistent B operands: K rows (P waves) or V rows (dS waves) of the wave's 32 keys
+  i16x8_t kvf[KK];
+  {
+    const __amdgpu_buffer_rsrc_t frs = make_rsrc((role == 0 ? K : V) + kv_off, head_bytes);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const uint32_t off = ((uint32_t)(kw + l32) * D + 16 * kk + 8 * g) * 2;
-    kf[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(krs, off));
-    vf[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(vrs, off));
+    for (int kk = 0; kk < KK; ++kk)
+      kvf[kk] = __builtin_bit_cast(i16x8_t, buffer_load16(frs, ((uint32_t)(kw + l32) * D + 16 * kk + 8 * g) * 2));
   }
   wait_all_loads();
-  f32x16_t dvacc[DB], dkacc[DB];
+  // dV^T (P waves) or dK^T (dS waves)
+  f32x16_t acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dvacc[db] = f32x16_t{};
-    dkacc[db] = f32x16_t{};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
   const int nqb = npad / kBwdRows;
   const int qstart = CAUSAL ? (k0 / kBwdRows) : 0;
@@ -246,9 +263,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int kDiag = kBwdKeys / kBwdRows;
 
   // loop-invariant offsets.  Reads (16-bit units): Q / dO rows 32qs + l32 at chunk 2kk + g;
-  // Q^T / dO^T rows 32db + l32 at chunk 4qs + 2t + g.  Direct loads (bytes): piece 4i + w of
-  // a tile, lane l -> LDS chunk 64(4i + w) + l, fetched from the logical chunk the swizzle
-  // puts there.
+  // Q^T / dO^T rows 32db + l32 at chunk 4qs + 2t + g.  Direct loads (bytes): piece NW i + w of
+  // a tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
   int off_row[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) off_row[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
@@ -258,10 +274,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
     for (int t = 0; t < 2; ++t) off_t[qs][t] = l32 * kBwdRows + (((4 * qs + 2 * t + g) ^ tsw) << 3);
-  uint32_t dma_qd[PIECES / 4], dma_tt[PIECES / 4];
+  uint32_t dma_qd[PW], dma_tt[PW];
 #pragma unroll
-  for (int i = 0; i < PIECES / 4; ++i) {
-    const int pch = 64 * (4 * i + w) + lane;
+  for (int i = 0; i < PW; ++i) {
+    const int pch = 64 * (NW * i + w) + lane;
     const int r = pch / CH, cc = pch % CH;
     dma_qd[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
     const int rt = pch / 8, ct = pch % 8;
@@ -273,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     h = kvh * G + hh;
     q0 = (qstart + it - hh * per_head) * kBwdRows;
   };
-  // direct loads of block it's four tiles into buffer `par`
+  // direct loads of block it's four tiles and its statistics into buffer `par`
   auto load_tiles = [&](int it, auto par) __attribute__((always_inline)) {
     int h, q0;
     block_of(it, h, q0);
@@ -287,136 +303,139 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     short* tt = TT(par);
     const uint32_t rowoff = (uint32_t)q0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < PIECES / 4; ++i) {
-      const int piece = 4 * i + w;
+    for (int i = 0; i < PW; ++i) {
+      const int piece = NW * i + wu;
       buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + rowoff);
       buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + rowoff);
       buffer_load16_lds(qtrs, tt + 512 * piece, dma_tt[i]);
       buffer_load16_lds(otrs, tt + TILE + 512 * piece, dma_tt[i]);
     }
-  };
-  // LSE2 and D of the 16 rows a lane needs in half qs of block it: rows 32qs + 8rr + 4g + e
-  auto load_stats = [&](int it, int qs, float4 (&l4)[4], float4 (&d4)[4]) __attribute__((always_inline)) {
-    int h, q0;
-    block_of(it, h, q0);
-    const size_t r0 = ((size_t)b * Hq + h) * npad + q0 + 32 * qs + 4 * g;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      l4[rr] = *(const float4*)(Lse2 + r0 + 8 * rr);
-      d4[rr] = *(const float4*)(Dsum + r0 + 8 * rr);
+    // 64 floats of LSE2 (wave 0) or -D (wave 1): lanes 0-15 carry them, the rest read past the
+    // 256-byte range and write zeros
+    if (wu < 2) {
+      const float* src = (wu == 0 ? Lse2 : Dneg) + bhq * npad + q0;
+      buffer_load16_lds(make_rsrc(src, kBwdRows * 4), (short*)(ST(par) + 256 * wu), 16 * lane);
     }
   };
 
-  // S = Q K^T, dP = dO V^T for rows 32qs .. 32qs+31 of the tile in buffer `par`; a lane owns
-  // key kw + l32 of the accumulator, register r holds query 32qs + 8(r/4) + 4g + r%4
-  auto s_dp = [&](auto par, int qs, f32x16_t& sacc, f32x16_t& dp) __attribute__((always_inline)) {
-    const short* Qs = QD(par) + 32 * qs * D;
-    const short* dOs = QD(par) + TILE + 32 * qs * D;
-    sacc = f32x16_t{};
-    dp = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const i16x8_t aq = __builtin_bit_cast(i16x8_t, *(const uint4*)(Qs + off_row[kk]));
-      const i16x8_t ado = __builtin_bit_cast(i16x8_t, *(const uint4*)(dOs + off_row[kk]));
-      sacc = mfma32x32x16<BF16>(aq, kf[kk], sacc);
-      dp = mfma32x32x16<BF16>(ado, vf[kk], dp);
-    }
-  };
-  // P = exp2(S c - LSE2) and dS = P (dP - D), packed as the B operands of dV^T and dK^T
-  auto p_ds = [&](int q0, int qs, f32x16_t& sacc, f32x16_t& dp, const float4 (&l4)[4], const float4 (&d4)[4],
-                  i16x8_t (&pb)[2], i16x8_t (&sb)[2], auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int key = kw + l32;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float lv[4] = {l4[rr].x, l4[rr].y, l4[rr].z, l4[rr].w};
-      const float dv4[4] = {d4[rr].x, d4[rr].y, d4[rr].z, d4[rr].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rr + e;
-        float p = __builtin_amdgcn_exp2f(sacc[r] * c - lv[e]);
-        if constexpr (MASK) {
-          if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
-        }
-        sacc[r] = p;
-        dp[r] = p * (dp[r] - dv4[e]);
-      }
-    }
-    pb[0] = pack8<BF16>(sacc, 0);
-    pb[1] = pack8<BF16>(sacc, 8);
-    sb[0] = pack8<BF16>(dp, 0);
-    sb[1] = pack8<BF16>(dp, 8);
-  };
-  // dV^T += dO^T P, dK^T += Q^T dS for rows 32qs .. (k = query rows 32qs + 16t + slot order)
-  auto dv_dk = [&](auto par, int qs, const i16x8_t (&pb)[2], const i16x8_t (&sb)[2]) __attribute__((always_inline)) {
-    const short* tq = TT(par);
-    const short* tdo = TT(par) + TILE;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int o = 32 * db * kBwdRows + off_t[qs][t];
-        const i16x8_t ado = __builtin_bit_cast(i16x8_t, *(const uint4*)(tdo + o));
-        dvacc[db] = mfma32x32x16<BF16>(ado, pb[t], dvacc[db]);
-        const i16x8_t aq = __builtin_bit_cast(i16x8_t, *(const uint4*)(tq + o));
-        dkacc[db] = mfma32x32x16<BF16>(aq, sb[t], dkacc[db]);
-      }
-    }
-  };
-
-  // One query block (tile in buffer `par`).  The statistics of half 0 were loaded during the
-  // previous step; those of half 1 are requested before the next block's tiles, so waiting for
-  // them never waits for the tiles.  Within the block, the S/dP MFMAs of half 1 are independent
-  // of the P/dS vector work of half 0, and the dV/dK MFMAs of half 0 of the vector work of
-  // half 1, which lets the scheduler overlap them.
-  float4 la[4], da[4], lb[4], db4[4];
+  // One query block in buffer `par` (the next one is loaded meanwhile into the other buffer).
   auto step = [&](int it, auto par, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     using Other = std::integral_constant<int, 1 - decltype(par)::value>;
-    const bool has_next = it + 1 < total;
     int h, q0;
     block_of(it, h, q0);
-    load_stats(it, 1, lb, db4);
-    if (has_next) load_tiles(it + 1, Other{});
-    f32x16_t x0, x1, y0, y1;
-    i16x8_t pb0[2], sb0[2], pb1[2], sb1[2];
-    s_dp(par, 0, x0, x1);
-    p_ds(q0, 0, x0, x1, la, da, pb0, sb0, mask_tag);
-    s_dp(par, 1, y0, y1);
-    p_ds(q0, 1, y0, y1, lb, db4, pb1, sb1, mask_tag);
-    dv_dk(par, 0, pb0, sb0);
-    // (on the last block this re-reads its own statistics: unused, and no branch splits the
-    // block of independent work)
-    load_stats(min(it + 1, total - 1), 0, la, da);
-    dv_dk(par, 1, pb1, sb1);
-    // scheduling: LDS reads run 4 ahead of their MFMAs (mask 0x100 = LDS reads, 0x008 = MFMA,
-    // 0x402 = vector ALU); the P/dS vector work of each half sits between the MFMAs of the next
-    // contraction
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // (the last block reloads itself into the idle buffer: no branch around the loads)
+    load_tiles(it + 1 < total ? it + 1 : it, Other{});
+    const short* qd = QD(par);
+    const short* tt = TT(par);
+    const float* st = ST(par);
+    // slots of the P exchange (16-byte units): [quarter][2 * half + t][lane]
+    uint4* px = pex + kq * 256 + lane;
+    if (role == 0) {
+      // ---- S = Q K^T for rows 0-31 and 32-63; a lane owns key kw + l32, register r holds
+      // row 32qs + 8(r/4) + 4g + r%4
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
-    }
+        for (int qs = 0; qs < 2; ++qs) {
+          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(qd + 32 * qs * D + off_row[kk]));
+          s[qs] = mfma32x32x16<BF16>(a, kvf[kk], s[qs]);
+        }
+      // ---- P = exp2(S c - LSE2), rounded to the input type: B operand of dV^T and the partner's dS
+      const int key = kw + l32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 l4 = *(const float4*)(st + 32 * qs + 8 * rr + 4 * g);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rr + e;
+            float p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
+            if constexpr (MASK) {
+              if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
+            }
+            s[qs][r] = p;
+          }
+        }
+      }
+      i16x8_t pb[2][2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pb[qs][t] = pack8<BF16>(s[qs], 8 * t);
+          px[64 * (2 * qs + t)] = __builtin_bit_cast(uint4, pb[qs][t]);
+        }
+      lds_barrier();   // P is visible to the dS waves
+      // ---- dV^T += dO^T P (slot (g, e) of half t is row 32qs + 16t + 8(e/4) + 4g + e%4)
+      const short* tdo = tt + TILE;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(tdo + 32 * db * kBwdRows + off_t[qs][t]));
+            acc[db] = mfma32x32x16<BF16>(a, pb[qs][t], acc[db]);
+          }
+    } else {
+      // ---- dP - D = dO V^T accumulated from -D (same layout as S)
+      f32x16_t dp[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 d4 = *(const float4*)(st + 256 + 32 * qs + 8 * rr + 4 * g);
+          dp[qs][4 * rr + 0] = d4.x;
+          dp[qs][4 * rr + 1] = d4.y;
+          dp[qs][4 * rr + 2] = d4.z;
+          dp[qs][4 * rr + 3] = d4.w;
+        }
+      const short* dos = qd + TILE;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(dos + 32 * qs * D + off_row[kk]));
+          dp[qs] = mfma32x32x16<BF16>(a, kvf[kk], dp[qs]);
+        }
+      lds_barrier();   // the partner's P has been written
+      // ---- dS = P (dP - D), packed as the B operand of dK^T
+      i16x8_t sb[2][2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+          const u32x4_t pw = __builtin_bit_cast(u32x4_t, px[64 * (2 * qs + t)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            dp[qs][r] *= lo_to_float<BF16>(pw[e]);
+            dp[qs][r + 1] *= hi_to_float<BF16>(pw[e]);
+          }
+          sb[qs][t] = pack8<BF16>(dp[qs], 8 * t);
+        }
+      // ---- dK^T += Q^T dS
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(tt + 32 * db * kBwdRows + off_t[qs][t]));
+            acc[db] = mfma32x32x16<BF16>(a, sb[qs][t], acc[db]);
+          }
     }
     // block it + 1 has landed and every wave is done with this block's buffers
     wait_all_loads();
     __syncthreads();
   };
 
-  if (total > 0) {
-    load_stats(0, 0, la, da);
-    load_tiles(0, Par0{});
-  }
+  if (total > 0) load_tiles(0, Par0{});
   wait_all_loads();
   __syncthreads();
   int it = 0;
@@ -451,20 +470,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
   const int key = kw + l32;
   if (key < N) {
-    uint16_t* dvp = dV + kv_off + (size_t)key * D;
-    uint16_t* dkp = dK + kv_off + (size_t)key * D;
+    uint16_t* dst = (role == 0 ? dV : dK) + kv_off + (size_t)key * D;
+    const float f = role == 0 ? 1.f : scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * db + 8 * rr + 4 * g;
-        uint2 pv, pk;
-        pv.x = pack2<BF16>(dvacc[db][4 * rr + 0], dvacc[db][4 * rr + 1]);
-        pv.y = pack2<BF16>(dvacc[db][4 * rr + 2], dvacc[db][4 * rr + 3]);
-        pk.x = pack2<BF16>(dkacc[db][4 * rr + 0] * scale, dkacc[db][4 * rr + 1] * scale);
-        pk.y = pack2<BF16>(dkacc[db][4 * rr + 2] * scale, dkacc[db][4 * rr + 3] * scale);
-        *(uint2*)(dvp + d0) = pv;
-        *(uint2*)(dkp + d0) = pk;
+        uint2 pk;
+        pk.x = pack2<BF16>(acc[db][4 * rr + 0] * f, acc[db][4 * rr + 1] * f);
+        pk.y = pack2<BF16>(acc[db][4 * rr + 2] * f, acc[db][4 * rr + 3] * f);
+        *(uint2*)(dst + d0) = pk;
       }
   }
 }
@@ -602,7 +618,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       if constexpr (MASK) {
         if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
       }
-      st[r] = p * (dpt[r] - dd);
+      st[r] = p * (dpt[r] + dd);
     }
     sb[0] = pack8<BF16>(st, 0);
     sb[1] = pack8<BF16>(st, 8);
@@ -732,7 +748,7 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
   const int nkb = (N + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(nkb * B * Hkv), dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
                      w.lse2, w.qt, w.dot, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e,
                      scale);

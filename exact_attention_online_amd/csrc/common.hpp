@@ -87,6 +87,24 @@ __device__ __forceinline__ float to_float(uint16_t x) {
   }
 }
 
+// The low / high 16-bit half of a packed pair as a float.
+template <bool BF16>
+__device__ __forceinline__ float lo_to_float(uint32_t pair) {
+  if constexpr (BF16) {
+    return __uint_as_float(pair << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFFu));
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ float hi_to_float(uint32_t pair) {
+  if constexpr (BF16) {
+    return __uint_as_float(pair & 0xFFFF0000u);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+  }
+}
+
 // max / sum of a value over lanes l and l ^ 32.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -146,6 +164,14 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, shor
 // prefetches, because the counters drain in order, which exposes the full load latency on
 // every iteration.
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier after this wave's LDS accesses have completed (s_waitcnt lgkmcnt(0);
+// s_barrier): makes LDS writes visible to the other waves without waiting for the direct
+// loads in flight, which a full __syncthreads() fence would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7: no wait; lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ i16x4_t ds_read_tr16(const short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);

@@ -101,7 +101,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     int causal, float softmax_scale, int dtype, attn_stream_t stream);
 
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
- * up to a multiple of 64: D = rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
+ * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
  * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and
  * [B,Hkv,Npad,d] (K), i.e. 2 * roundup(4 * B * Hq * Npad, 256) + 2 * (2 * Hq + Hkv) * B * Npad * d
  * bytes.  0 if the sizes are invalid. */
@@ -124,7 +124,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
  * streams once preprocess is complete) produces exactly what attn_bwd produces; attn_bwd is
  * these three calls on one stream.
- *   attn_bwd_preprocess: D = rowsum(dO * O), LSE * log2(e) and the transposed tiles of q,
+ *   attn_bwd_preprocess: -D = -rowsum(dO * O), LSE * log2(e) and the transposed tiles of q,
  *                        dout and k into the workspace.
  *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
  *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
