@@ -284,48 +284,56 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     dma_tt[i] = ((uint32_t)rt * kBwdRows + ((ct ^ ((rt >> 1) & 7)) << 3)) * 2;
   }
 
-  auto block_of = [&](int it, int& h, int& q0) __attribute__((always_inline)) {
-    const int hh = it / per_head;
-    h = kvh * G + hh;
-    q0 = (qstart + it - hh * per_head) * kBwdRows;
+  // Loader state: the block that the next call of load_next fetches (query head ld_hh of the
+  // group, rows ld_q0 ..), and buffer descriptors over that head's Q, dO, transposed tiles and
+  // statistics, rebuilt only when the head changes.
+  int ld_hh = 0, ld_q0 = qstart * kBwdRows, ld_left = per_head;
+  __amdgpu_buffer_rsrc_t qrs, ors, qtrs, otrs, srs;
+  auto head_rsrcs = [&]() __attribute__((always_inline)) {
+    const size_t bhq = (size_t)b * Hq + kvh * G + ld_hh;
+    qrs = make_rsrc(Q + bhq * N * D, head_bytes);
+    ors = make_rsrc(dO + bhq * N * D, head_bytes);
+    qtrs = make_rsrc(QT + bhq * nqb * TILE, (uint32_t)nqb * TILE * 2);
+    otrs = make_rsrc(dOT + bhq * nqb * TILE, (uint32_t)nqb * TILE * 2);
+    // LSE2 (wave 0) or -D (wave 1) of the head's rows
+    srs = make_rsrc((wu == 0 ? Lse2 : Dneg) + bhq * npad, (uint32_t)npad * 4);
   };
-  // direct loads of block it's four tiles and its statistics into buffer `par`
-  auto load_tiles = [&](int it, auto par) __attribute__((always_inline)) {
-    int h, q0;
-    block_of(it, h, q0);
-    const size_t bhq = (size_t)b * Hq + h;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + bhq * N * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + bhq * N * D, head_bytes);
-    const size_t toff = (bhq * nqb + q0 / kBwdRows) * TILE;
-    const __amdgpu_buffer_rsrc_t qtrs = make_rsrc(QT + toff, TILE * 2);
-    const __amdgpu_buffer_rsrc_t otrs = make_rsrc(dOT + toff, TILE * 2);
+  head_rsrcs();
+  // direct loads of the loader's block into buffer `par` (four tiles, and the 64 rows' LSE2
+  // and -D from waves 0 and 1, whose lanes 16-63 fetch rows that are never read), then advance
+  // the loader; after the last block it stays there, so the last step reloads it into the idle
+  // buffer instead of branching around the loads
+  auto load_next = [&](auto par) __attribute__((always_inline)) {
     short* qd = QD(par);
     short* tt = TT(par);
-    const uint32_t rowoff = (uint32_t)q0 * D * 2;
+    // a row-major tile of rows q0.. and transposed tile q0 / 64 start at the same byte offset
+    const uint32_t off = (uint32_t)ld_q0 * D * 2;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int piece = NW * i + wu;
-      buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + rowoff);
-      buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + rowoff);
-      buffer_load16_lds(qtrs, tt + 512 * piece, dma_tt[i]);
-      buffer_load16_lds(otrs, tt + TILE + 512 * piece, dma_tt[i]);
+      buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + off);
+      buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + off);
+      buffer_load16_lds(qtrs, tt + 512 * piece, dma_tt[i] + off);
+      buffer_load16_lds(otrs, tt + TILE + 512 * piece, dma_tt[i] + off);
     }
-    // 64 floats of LSE2 (wave 0) or -D (wave 1): lanes 0-15 carry them, the rest read past the
-    // 256-byte range and write zeros
-    if (wu < 2) {
-      const float* src = (wu == 0 ? Lse2 : Dneg) + bhq * npad + q0;
-      buffer_load16_lds(make_rsrc(src, kBwdRows * 4), (short*)(ST(par) + 256 * wu), 16 * lane);
+    if (wu < 2) buffer_load16_lds(srs, (short*)(ST(par) + 256 * wu), 16 * lane + (uint32_t)ld_q0 * 4);
+    if (ld_left > 1) {
+      --ld_left;
+      ld_q0 += kBwdRows;
+    } else if (ld_hh + 1 < G) {
+      ++ld_hh;
+      ld_q0 = qstart * kBwdRows;
+      ld_left = per_head;
+      head_rsrcs();
     }
   };
 
-  // One query block in buffer `par` (the next one is loaded meanwhile into the other buffer).
-  auto step = [&](int it, auto par, auto mask_tag) __attribute__((always_inline)) {
+  // One query block (rows q0 ..) in buffer `par`; the next one is loaded meanwhile into the
+  // other buffer.
+  auto step = [&](int q0, auto par, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     using Other = std::integral_constant<int, 1 - decltype(par)::value>;
-    int h, q0;
-    block_of(it, h, q0);
-    // (the last block reloads itself into the idle buffer: no branch around the loads)
-    load_tiles(it + 1 < total ? it + 1 : it, Other{});
+    load_next(Other{});
     const short* qd = QD(par);
     const short* tt = TT(par);
     const float* st = ST(par);
@@ -435,36 +443,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     __syncthreads();
   };
 
-  if (total > 0) load_tiles(0, Par0{});
+  if (total > 0) load_next(Par0{});
   wait_all_loads();
   __syncthreads();
   int it = 0;
-  // steps [it, end) with the buffer parity of each step fixed at compile time
-  auto run = [&](int end, auto mask_tag) __attribute__((always_inline)) {
+  // unmasked steps [it, end) with the buffer parity of each step fixed at compile time
+  auto run = [&](int end) __attribute__((always_inline)) {
     if ((it & 1) && it < end) {
-      step(it, Par1{}, mask_tag);
+      step(0, Par1{}, std::false_type{});
       ++it;
     }
     for (; it + 1 < end; it += 2) {
-      step(it, Par0{}, mask_tag);
-      step(it + 1, Par1{}, mask_tag);
+      step(0, Par0{}, std::false_type{});
+      step(0, Par1{}, std::false_type{});
     }
     if (it < end) {
-      step(it, Par0{}, mask_tag);
+      step(0, Par0{}, std::false_type{});
       ++it;
     }
   };
   if constexpr (CAUSAL) {
     for (int hh = 0; hh < G; ++hh) {
-      const int diag_end = min(hh * per_head + kDiag, (hh + 1) * per_head);
+      const int base = hh * per_head;
+      const int diag_end = min(base + kDiag, base + per_head);
       for (; it < diag_end; ++it) {
-        if (it & 1) step(it, Par1{}, std::true_type{});
-        else step(it, Par0{}, std::true_type{});
+        const int q0 = (qstart + it - base) * kBwdRows;
+        if (it & 1) step(q0, Par1{}, std::true_type{});
+        else step(q0, Par0{}, std::true_type{});
       }
-      run((hh + 1) * per_head, std::false_type{});
+      run(base + per_head);
     }
   } else {
-    run(total, std::false_type{});
+    run(total);
   }
 
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
