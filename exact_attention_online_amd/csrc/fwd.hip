@@ -8,9 +8,12 @@
 // workgroup are skipped and only blocks crossing the diagonal are masked.
 //
 // gfx950 mapping
-//   * grid: one workgroup per (batch, query head, block of BR = 4 * QB * 32 query rows);
-//     the 4 waves each own QB * 32 query rows.  Causal launches visit the longest query blocks
-//     first (block ids count down), so short blocks fill the tail of the schedule.
+//   * grid: one workgroup per (batch, query head, block of BR = NWV * QB * 32 query rows);
+//     the NWV waves each own QB * 32 query rows.  The plain forward runs 8 waves (256 rows,
+//     one workgroup and two waves per SIMD on a CU), so each K/V tile loaded into LDS serves
+//     256 query rows; the variants with window/ALiBi (more registers) and variable lengths
+//     (finer early exit) run 4.  Causal launches visit the longest query blocks first (block
+//     ids count down), so short blocks fill the tail of the schedule.
 //   * transposed formulation: each wave computes S^T = K Q^T and O^T = V^T P^T with
 //     v_mfma_f32_32x32x16.  In the S^T accumulator a lane owns one query (column l % 32) and 16
 //     keys, so the row maximum and row sum are lane-local; one v_permlane32_swap combines the
@@ -65,16 +68,16 @@ struct FwdTile {
 // [H, T, d] and LSE [H, T] with T = N_in packed tokens; sequence b is rows cu_seqlens[b] ..
 // cu_seqlens[b + 1] - 1 of every head (clamped to [0, T]) and attends only within itself.  The
 // grid covers the longest sequence (nqb blocks of BR rows); blocks past a sequence's end exit.
-template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false, bool VARLEN = false>
-__global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
+template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false, bool VARLEN = false, int NWV = 4>
+__global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N_in, int BH, int nqb,
     float c /* softmax_scale * log2(e) */, int window, const float* __restrict__ slopes, float inv_scale,
     const int* __restrict__ cu_seqlens) {
   using T = FwdTile<D, BC>;
   constexpr int CH = T::CH, KK = D / 16, DB = D / 32, KB = BC / 32;
-  constexpr int BR = 4 * QB * 32;
-  static_assert(T::PIECES % 4 == 0, "each wave moves the same number of pieces");
+  constexpr int BR = NWV * QB * 32;
+  static_assert(T::PIECES % NWV == 0, "each wave moves the same number of pieces");
   // four distinct LDS objects, so that the compiler can tell a direct load into one buffer from
   // a read of another and does not wait for the load before the read
   __shared__ __attribute__((aligned(1024))) short k_lds0[T::ELEMS];
@@ -155,17 +158,17 @@ __global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, (uint32_t)N * D * 2);
   // direct loads: piece p = 4i + w of a tile; lane l fills LDS chunk 64p + l (row (64p + l) / CH,
   // physical chunk l % CH) with the logical chunk that the swizzle puts there
-  uint32_t goff[T::PIECES / 4];
+  uint32_t goff[T::PIECES / NWV];
 #pragma unroll
-  for (int i = 0; i < T::PIECES / 4; ++i) {
-    const int p = 64 * (4 * i + w) + lane;
+  for (int i = 0; i < T::PIECES / NWV; ++i) {
+    const int p = 64 * (NWV * i + w) + lane;
     const int row = p / CH, pch = p % CH;
     goff[i] = ((uint32_t)row * D + ((pch ^ swz<D>(row)) << 3)) * 2;
   }
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, short* dst, int kt0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < T::PIECES / 4; ++i)
-      buffer_load16_lds(rs, dst + 512 * (4 * i + w), goff[i] + (uint32_t)kt0 * D * 2);
+    for (int i = 0; i < T::PIECES / NWV; ++i)
+      buffer_load16_lds(rs, dst + 512 * (NWV * i + w), goff[i] + (uint32_t)kt0 * D * 2);
   };
 
   // loop-invariant LDS offsets (16-bit units): K rows l32 (+32 kb) at chunk 2kk + g; V^T
@@ -428,11 +431,12 @@ __global__ __launch_bounds__(256, EXT ? 1 : 2) void attn_fwd_kernel(
 template <bool BF16, int D, int QB, int BC, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                int Hkv, int N, float scale, hipStream_t stream) {
-  constexpr int BR = 4 * QB * 32;
+  constexpr int NWV = 8;
+  constexpr int BR = NWV * QB * 32;
   const int nqb = (N + BR - 1) / BR;
   const int BH = B * Hq;
-  auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL>;
-  hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(256), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+  auto kern = attn_fwd_kernel<BF16, D, QB, BC, CAUSAL, false, false, NWV>;
+  hipLaunchKernelGGL(kern, dim3(nqb * BH), dim3(NWV * 64), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e, 0,
                      (const float*)nullptr, 1.f, (const int*)nullptr);
   return hipGetLastError();
