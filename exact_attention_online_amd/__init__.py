@@ -12,12 +12,12 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "fwd_varlen", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
-           "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
+           "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
            "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,10 @@ def load():
     lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 7 + [f, i, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_ext.restype = i
+    lib.attn_bwd_varlen_workspace_size.argtypes = [i] * 5
+    lib.attn_bwd_varlen_workspace_size.restype = sz
+    lib.attn_bwd_varlen.argtypes = [vp] * 10 + [i] * 7 + [f, i, vp, sz, vp]
+    lib.attn_bwd_varlen.restype = i
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i] * 7
     lib.attn_fwd_splitkv_workspace_size.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, sz, vp]
@@ -240,6 +244,48 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_varlen_workspace_size(B, Hq, Hkv, max_seqlen, d) -> int:
+    return int(load().attn_bwd_varlen_workspace_size(B, Hq, Hkv, max_seqlen, d))
+
+
+def bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+               workspace=None, dq=None, dk=None, dv=None):
+    """dQ [Hq,T,d], dK, dV [Hkv,T,d] for sequences packed along T, with o, lse from fwd_varlen (same
+    cu_seqlens, max_seqlen, causal flag and scale).  Rows outside every sequence come back as zeros
+    when the outputs are allocated here."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise AttnError(f"expected q [Hq,T,d], k/v [Hkv,T,d]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    if k.shape[1] != T or k.shape[2] != d:
+        raise AttnError("q and k/v disagree in T or d")
+    for t in (q, k, v, o, do):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise AttnError("q, k, v, o, do must be contiguous device tensors of one dtype on one device")
+    for t in (o, do):
+        if t.shape != q.shape:
+            raise AttnError("o and do must match q in shape")
+    if lse.shape != (Hq, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise AttnError("lse must be float32 [Hq,T]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise AttnError("cu_seqlens must be an int32 device tensor [B+1]")
+    B = cu_seqlens.numel() - 1
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = bwd_varlen_workspace_size(B, Hq, Hkv, int(max_seqlen), d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.zeros_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
+    _check(load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(cu_seqlens.contiguous()), B, Hq, Hkv, T, int(max_seqlen), d,
+                                  int(bool(causal)), scale, dt, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -13,13 +13,14 @@ namespace eao {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int N, int d, bool causal, float scale, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
-                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream);
+                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream,
+                          int max_seqlen = 0, const int* cu = nullptr);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                           const void* workspace, hipStream_t stream);
+                           const void* workspace, hipStream_t stream, int max_seqlen = 0, const int* cu = nullptr);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                          int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                         const void* workspace, hipStream_t stream);
+                         const void* workspace, hipStream_t stream, int max_seqlen = 0, const int* cu = nullptr);
 hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                           int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
                           hipStream_t stream);
@@ -191,6 +192,41 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_ERR_HIP;
   if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s) !=
       hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+size_t attn_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int max_seqlen, int d) {
+  if (check_sizes(B, Hq, Hkv, max_seqlen, d) != ATTN_OK) return 0;
+  return eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d);
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int Hq, int Hkv, int T,
+                    int max_seqlen, int d, int causal, float softmax_scale, int dtype, void* workspace,
+                    size_t workspace_bytes, attn_stream_t stream) {
+  for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return ATTN_ERR_INVALID;
+  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u) != 0) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale) || max_seqlen < 1 || max_seqlen > T) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  // the packed tensors are one batch of T rows per head; the workspace is B sequences of max_seqlen
+  int st = check_sizes(1, Hq, Hkv, T, d);
+  if (st != ATTN_OK) return st;
+  st = check_sizes(B, Hq, Hkv, max_seqlen, d);
+  if (st != ATTN_OK) return st;
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d)) return ATTN_ERR_WORKSPACE;
+  const bool bf16 = dtype == ATTN_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, T, d, bf16, workspace, s, max_seqlen, cu_seqlens) !=
+      hipSuccess)
+    return ATTN_ERR_HIP;
+  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, workspace,
+                           s, max_seqlen, cu_seqlens) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, workspace, s,
+                         max_seqlen, cu_seqlens) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

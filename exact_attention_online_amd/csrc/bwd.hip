@@ -60,6 +60,18 @@ constexpr int kDqKeys = 64;     // keys per dQ step
 // queries of every group of 16 permuted (position 8g + e holds query 8(e/4) + 4g + e%4): a
 // 16-byte read at position 8g then matches the order in which an MFMA accumulator holds the
 // probabilities, so the transposed operands of dV and dK are plain row reads.
+// Row range of sequence b in a packed variable-length batch: cu_seqlens entries clamped to
+// [0, T] and made non-decreasing, and the length capped at the workspace rows per head (npad),
+// so that a malformed array cannot send a kernel outside its buffers.
+struct SeqRange {
+  int s0, n;
+};
+__device__ __forceinline__ SeqRange seq_range(const int* __restrict__ cu, int b, int T, int npad) {
+  const int s0 = min(max(cu[b], 0), T);
+  const int s1 = min(max(cu[b + 1], s0), T);
+  return SeqRange{s0, min(s1 - s0, npad)};
+}
+
 struct BwdWs {
   float* dsum;
   float* lse2;
@@ -115,13 +127,19 @@ __device__ __forceinline__ void write_transposed(const uint16_t* t, uint16_t* __
 // tile's rows, and the tiles of Q and dO written transposed.  Workgroups after that: one
 // (batch * K/V head, 64-row tile) each, the tile of K written transposed.  Rows past N are
 // zeros.  Loads: 16-byte chunk tid + 256 i of the tile, so each wave reads whole rows.
-template <bool BF16, int D>
+//
+// VARLEN: sequences packed without padding, Q/O/dO [Hq,T,d], K [Hkv,T,d], LSE [Hq,T] (T = N_in
+// rows), sequence b = rows cu_seqlens[b] .. cu_seqlens[b+1]-1; the workspace keeps the
+// [B*H][npad] layout with npad from the longest sequence, and tiles past a sequence's end are
+// neither read nor written.
+template <bool BF16, int D, bool VARLEN = false>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                                                       const uint16_t* __restrict__ K, float* __restrict__ Dsum,
                                                       float* __restrict__ Lse2, uint16_t* __restrict__ QT,
-                                                      uint16_t* __restrict__ dOT, uint16_t* __restrict__ KT, int N,
-                                                      int npad, int nq_blocks) {
+                                                      uint16_t* __restrict__ dOT, uint16_t* __restrict__ KT, int N_in,
+                                                      int npad, int nq_blocks, int Hq, int Hkv,
+                                                      const int* __restrict__ cu_seqlens) {
   constexpr int STR = D + 8;                 // padded LDS row (16-bit elements)
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int CPT = kBwdRows * CH / 256;   // chunks per thread per tile
@@ -131,7 +149,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if ((int)blockIdx.x >= nq_blocks) {
     const int idx = blockIdx.x - nq_blocks;
     const int bkv = idx / ntile, tile = idx % ntile;
-    const uint16_t* src = K + ((size_t)bkv * N + (size_t)tile * kBwdRows) * D;
+    int N = N_in;
+    size_t row0 = (size_t)bkv * N_in;
+    if constexpr (VARLEN) {
+      const SeqRange sr = seq_range(cu_seqlens, bkv / Hkv, N_in, npad);
+      if (tile * kBwdRows >= sr.n) return;
+      N = sr.n;
+      row0 = (size_t)(bkv % Hkv) * N_in + sr.s0;
+    }
+    const uint16_t* src = K + (row0 + (size_t)tile * kBwdRows) * D;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
@@ -144,7 +170,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     return;
   }
   const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
-  const size_t base = ((size_t)bh * N + (size_t)tile * kBwdRows) * D;
+  int N = N_in;
+  size_t row0 = (size_t)bh * N_in;             // first row of the head (sequence) in Q, O, dO, LSE
+  if constexpr (VARLEN) {
+    const SeqRange sr = seq_range(cu_seqlens, bh / Hq, N_in, npad);
+    if (tile * kBwdRows >= sr.n) return;
+    N = sr.n;
+    row0 = (size_t)(bh % Hq) * N_in + sr.s0;
+  }
+  const size_t base = (row0 + (size_t)tile * kBwdRows) * D;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
@@ -166,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     if (ch == 0) {
       const size_t r = (size_t)bh * npad + q;
       Dsum[r] = q < N ? -acc : 0.f;
-      Lse2[r] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+      Lse2[r] = q < N ? LSE[row0 + q] * kLog2e : INFINITY;
     }
     *(uint4*)(tq + row * STR + 8 * ch) = qv;
     *(uint4*)(tdo + row * STR + 8 * ch) = dv;
@@ -191,13 +225,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // [Q^T | dO^T] ([D rows][64], chunk c of row r at c ^ ((r / 2) % 8)), and LSE2 and -D of the
 // 64 rows, go straight from HBM into double-buffered LDS (direct buffer -> LDS loads one step
 // ahead, each buffer a distinct LDS object); every operand read is a 16-byte row read.
-template <bool BF16, int D, bool CAUSAL>
+// VARLEN: packed sequences as in bwd_pre_kernel (K/V/dK/dV [Hkv,T,d], Q/dO [Hq,T,d]); a key block
+// past its sequence's end exits at once.
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int npad, int nkb, float c /* scale * log2(e) */,
-    float scale) {
+    uint16_t* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
+    float scale, const int* __restrict__ cu_seqlens) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = 8;                              // waves per workgroup
   constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
@@ -238,7 +274,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int k0 = kblk * kBwdKeys;
   const int kw = k0 + 32 * kq;                      // this wave's first key
-  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
+  int N = N_in, s0 = 0;
+  if constexpr (VARLEN) {
+    const SeqRange sr = seq_range(cu_seqlens, b, N_in, npad);
+    if (k0 >= sr.n) return;                         // the whole workgroup: no barrier reached
+    N = sr.n;
+    s0 = sr.s0;
+  }
+  // first row of a head (of this sequence) in the [B,H,N,d] or packed [H,T,d] tensors
+  auto head_row0 = [&](int bh_b, int hh) -> size_t __attribute__((always_inline)) {
+    if constexpr (VARLEN) return (size_t)hh * N_in + s0;
+    else return (size_t)bh_b * N;
+  };
+  const size_t kv_off = head_row0(b * Hkv + kvh, kvh) * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
   // persistent B operands: K rows (P waves) or V rows (dS waves) of the wave's 32 keys
@@ -255,7 +303,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
-  const int nqb = npad / kBwdRows;
+  const int nqb = (N + kBwdRows - 1) / kBwdRows;   // query tiles of the sequence
+  const int nqb_ws = npad / kBwdRows;              // tiles per head in the workspace
   const int qstart = CAUSAL ? (k0 / kBwdRows) : 0;
   const int per_head = nqb - qstart;
   const int total = G * per_head;
@@ -291,10 +340,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   __amdgpu_buffer_rsrc_t qrs, ors, qtrs, otrs, srs;
   auto head_rsrcs = [&]() __attribute__((always_inline)) {
     const size_t bhq = (size_t)b * Hq + kvh * G + ld_hh;
-    qrs = make_rsrc(Q + bhq * N * D, head_bytes);
-    ors = make_rsrc(dO + bhq * N * D, head_bytes);
-    qtrs = make_rsrc(QT + bhq * nqb * TILE, (uint32_t)nqb * TILE * 2);
-    otrs = make_rsrc(dOT + bhq * nqb * TILE, (uint32_t)nqb * TILE * 2);
+    const size_t qoff = head_row0((int)bhq, kvh * G + ld_hh) * D;
+    qrs = make_rsrc(Q + qoff, head_bytes);
+    ors = make_rsrc(dO + qoff, head_bytes);
+    qtrs = make_rsrc(QT + bhq * nqb_ws * TILE, (uint32_t)nqb * TILE * 2);
+    otrs = make_rsrc(dOT + bhq * nqb_ws * TILE, (uint32_t)nqb * TILE * 2);
     // LSE2 (wave 0) or -D (wave 1) of the head's rows
     srs = make_rsrc((wu == 0 ? Lse2 : Dneg) + bhq * npad, (uint32_t)npad * 4);
   };
@@ -501,12 +551,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // of buffers distinct LDS objects, filled by direct buffer -> LDS loads: [K | V] ([64][D],
 // chunks swizzled by swz) and K^T ([D][64] from the preprocess, chunk c of row r at
 // c ^ ((r / 2) % 8)).  All LDS reads are 16-byte rows.
-template <bool BF16, int D, bool CAUSAL>
+// VARLEN: packed sequences as in bwd_pre_kernel; a query block past its sequence's end exits at
+// once.
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
-    const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int npad, int BH, int nqb,
-    float c /* scale * log2(e) */, float scale) {
+    const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
+    float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = kDqRows / 32;                  // waves per workgroup
   constexpr int TILE = kDqKeys * D;                 // 16-bit elements per tile
@@ -532,8 +584,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   const int bkv = b * Hkv + kvh;
-  const size_t q_row0 = (size_t)bh * N;
-  const size_t kv_off = (size_t)bkv * N * D;
+  int N = N_in;
+  size_t q_row0 = (size_t)bh * N_in;                // first row of the head in Q, dO, dQ
+  size_t kv_off = (size_t)bkv * N_in * D;
+  if constexpr (VARLEN) {
+    const SeqRange sr = seq_range(cu_seqlens, b, N_in, npad);
+    if (qblk * kDqRows >= sr.n) return;              // the whole workgroup: no barrier reached
+    N = sr.n;
+    q_row0 = (size_t)h * N_in + sr.s0;
+    kv_off = ((size_t)kvh * N_in + sr.s0) * D;
+  }
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + q_row0 * D, head_bytes);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + q_row0 * D, head_bytes);
@@ -738,82 +798,101 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool BF16, int D>
+// Dense launches: N rows per head, workspace sized by N.  Variable-length launches (cu != nullptr):
+// T packed rows per head in the tensors (passed as N), workspace and grid sized by max_seqlen.
+template <bool BF16, int D, bool VARLEN>
 static hipError_t launch_pre_t(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
-                               int Hq, int Hkv, int N, void* workspace, hipStream_t stream) {
-  const BwdWs w = bwd_ws(workspace, B, Hq, N, D);
+                               int Hq, int Hkv, int N, int max_seqlen, const int* cu, void* workspace,
+                               hipStream_t stream) {
+  const BwdWs w = bwd_ws(workspace, B, Hq, VARLEN ? max_seqlen : N, D);
   const int ntile = w.npad / kBwdRows;
   const int nq_blocks = B * Hq * ntile;
   const unsigned grid = (unsigned)(nq_blocks + B * Hkv * ntile);
-  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)q,
+  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D, VARLEN>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)o, (const uint16_t*)dout, lse, (const uint16_t*)k, w.dsum, w.lse2, w.qt, w.dot,
-                     w.kt, N, w.npad, nq_blocks);
+                     w.kt, N, w.npad, nq_blocks, Hq, Hkv, cu);
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
-                                hipStream_t stream) {
+                                void* dk, void* dv, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu,
+                                float scale, const void* workspace, hipStream_t stream) {
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
-  const int nkb = (N + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
+  const int rows = VARLEN ? max_seqlen : N;
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
+  const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
                      w.lse2, w.qt, w.dot, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e,
-                     scale);
+                     scale, cu);
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                              void* dq, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
-                              hipStream_t stream) {
+                              void* dq, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu, float scale,
+                              const void* workspace, hipStream_t stream) {
   (void)lse;
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, N, D);
-  const int nqb = (N + kDqRows - 1) / kDqRows;
+  const int rows = VARLEN ? max_seqlen : N;
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
+  const int nqb = (rows + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
-                     w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale);
+                     w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
-                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream) {
-  if (bf16) return d == 128 ? launch_pre_t<true, 128>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream)
-                            : launch_pre_t<true, 64>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream);
-  return d == 128 ? launch_pre_t<false, 128>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream)
-                  : launch_pre_t<false, 64>(q, k, o, dout, lse, B, Hq, Hkv, N, workspace, stream);
+                          int Hq, int Hkv, int N, int d, bool bf16, void* workspace, hipStream_t stream,
+                          int max_seqlen, const int* cu) {
+  if (cu != nullptr) {
+    if (bf16) return d == 128 ? launch_pre_t<true, 128, true>(q, k, o, dout, lse, B, Hq, Hkv, N, max_seqlen, cu, workspace, stream)
+                              : launch_pre_t<true, 64, true>(q, k, o, dout, lse, B, Hq, Hkv, N, max_seqlen, cu, workspace, stream);
+    return d == 128 ? launch_pre_t<false, 128, true>(q, k, o, dout, lse, B, Hq, Hkv, N, max_seqlen, cu, workspace, stream)
+                    : launch_pre_t<false, 64, true>(q, k, o, dout, lse, B, Hq, Hkv, N, max_seqlen, cu, workspace, stream);
+  }
+  if (bf16) return d == 128 ? launch_pre_t<true, 128, false>(q, k, o, dout, lse, B, Hq, Hkv, N, N, cu, workspace, stream)
+                            : launch_pre_t<true, 64, false>(q, k, o, dout, lse, B, Hq, Hkv, N, N, cu, workspace, stream);
+  return d == 128 ? launch_pre_t<false, 128, false>(q, k, o, dout, lse, B, Hq, Hkv, N, N, cu, workspace, stream)
+                  : launch_pre_t<false, 64, false>(q, k, o, dout, lse, B, Hq, Hkv, N, N, cu, workspace, stream);
 }
 
-#define EAO_DISPATCH(FN, ...)                                                                 \
+#define EAO_DISPATCH_V(FN, VL, ...)                                                           \
   if (bf16) {                                                                                 \
     if (d == 128) {                                                                           \
-      if (causal) return FN<true, 128, true>(__VA_ARGS__);                                    \
-      return FN<true, 128, false>(__VA_ARGS__);                                               \
+      if (causal) return FN<true, 128, true, VL>(__VA_ARGS__);                                \
+      return FN<true, 128, false, VL>(__VA_ARGS__);                                           \
     }                                                                                         \
-    if (causal) return FN<true, 64, true>(__VA_ARGS__);                                       \
-    return FN<true, 64, false>(__VA_ARGS__);                                                  \
+    if (causal) return FN<true, 64, true, VL>(__VA_ARGS__);                                   \
+    return FN<true, 64, false, VL>(__VA_ARGS__);                                              \
   }                                                                                           \
   if (d == 128) {                                                                             \
-    if (causal) return FN<false, 128, true>(__VA_ARGS__);                                     \
-    return FN<false, 128, false>(__VA_ARGS__);                                                \
+    if (causal) return FN<false, 128, true, VL>(__VA_ARGS__);                                 \
+    return FN<false, 128, false, VL>(__VA_ARGS__);                                            \
   }                                                                                           \
-  if (causal) return FN<false, 64, true>(__VA_ARGS__);                                        \
-  return FN<false, 64, false>(__VA_ARGS__);
+  if (causal) return FN<false, 64, true, VL>(__VA_ARGS__);                                    \
+  return FN<false, 64, false, VL>(__VA_ARGS__);
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                           const void* workspace, hipStream_t stream) {
-  EAO_DISPATCH(launch_dkdv_t, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, scale, workspace, stream)
+                           const void* workspace, hipStream_t stream, int max_seqlen, const int* cu) {
+  if (cu != nullptr) {
+    EAO_DISPATCH_V(launch_dkdv_t, true, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, max_seqlen, cu, scale, workspace,
+                   stream)
+  }
+  EAO_DISPATCH_V(launch_dkdv_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, cu, scale, workspace, stream)
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                          int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                         const void* workspace, hipStream_t stream) {
-  EAO_DISPATCH(launch_dq_t, q, k, v, dout, lse, dq, B, Hq, Hkv, N, scale, workspace, stream)
+                         const void* workspace, hipStream_t stream, int max_seqlen, const int* cu) {
+  if (cu != nullptr) {
+    EAO_DISPATCH_V(launch_dq_t, true, q, k, v, dout, lse, dq, B, Hq, Hkv, N, max_seqlen, cu, scale, workspace, stream)
+  }
+  EAO_DISPATCH_V(launch_dq_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, cu, scale, workspace, stream)
 }
-#undef EAO_DISPATCH
+#undef EAO_DISPATCH_V
 
 }  // namespace eao

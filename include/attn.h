@@ -100,6 +100,26 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     const int* cu_seqlens, int B, int Hq, int Hkv, int T, int max_seqlen, int d,
                     int causal, float softmax_scale, int dtype, attn_stream_t stream);
 
+/* Backward of attn_fwd_varlen: gradients of L = <O, dO> for variable-length sequences packed
+ * without padding ("FlashAttention-2: Faster Attention with Better Parallelism and Work
+ * Partitioning", OpenReview discussion, author responses: concatenated sequences and an array of
+ * lengths; "FlashAttention (NeurIPS 2022)" notes, "Backward - Recomputation").  Each sequence's
+ * gradients are those attn_bwd gives for that sequence alone.
+ *   q, o, dout [Hq,T,d], k, v [Hkv,T,d] in `dtype` (ATTN_F16 / ATTN_BF16), lse [Hq,T] float from
+ *   attn_fwd_varlen with the same cu_seqlens, causal flag and scale; cu_seqlens, B, T and
+ *   max_seqlen as for attn_fwd_varlen.  Outputs dq [Hq,T,d], dk, dv [Hkv,T,d] in `dtype`, dk and
+ *   dv summed over the query heads that share each K/V head; rows that belong to no sequence
+ *   (past cu_seqlens[B]) are not written.
+ *   workspace: device memory of at least attn_bwd_varlen_workspace_size() bytes, 256-byte
+ *   aligned, owned by the caller; clobbered.  A sequence longer than max_seqlen (rounded up to
+ *   64) gets unspecified gradients but no access outside the buffers.
+ * Returns an attn_status_t. */
+size_t attn_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int max_seqlen, int d);
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B,
+                    int Hq, int Hkv, int T, int max_seqlen, int d, int causal, float softmax_scale,
+                    int dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
  * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
  * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and

@@ -142,3 +142,26 @@ def test_fwd_varlen_rejects_bad_arguments():
     assert lib.attn_fwd_varlen(*bad) == 2
     bad = list(a); bad[14] = 2                                               # fp8
     assert lib.attn_fwd_varlen(*bad) == 2
+
+
+def test_bwd_varlen_rejects_bad_arguments():
+    lib = eao.load()
+    # q, k, v, o, dout, lse, dq, dk, dv, cu, B, Hq, Hkv, T, max_seqlen, d, causal, scale, dtype, ws, bytes, stream
+    need = lib.attn_bwd_varlen_workspace_size(3, 4, 2, 500, 128)
+    assert need == lib.attn_bwd_workspace_size(3, 4, 2, 500, 128) > 0
+    a = [P] * 10 + [3, 4, 2, 1000, 500, 128, 1, 0.1, 1, P, need, NULL]
+    bad = list(a); bad[9] = NULL                                             # no offsets
+    assert lib.attn_bwd_varlen(*bad) == 1
+    bad = list(a); bad[14] = 1001                                            # max_seqlen > T
+    assert lib.attn_bwd_varlen(*bad) == 1
+    bad = list(a); bad[15] = 96                                              # head dim
+    assert lib.attn_bwd_varlen(*bad) == 2
+    bad = list(a); bad[18] = 2                                               # fp8
+    assert lib.attn_bwd_varlen(*bad) == 2
+    bad = list(a); bad[20] = need - 1                                        # workspace too small
+    assert lib.attn_bwd_varlen(*bad) == 3
+    bad = list(a); bad[19] = NULL                                            # no workspace
+    assert lib.attn_bwd_varlen(*bad) == 3
+    bad = list(a); bad[12] = 3                                               # Hq % Hkv != 0
+    assert lib.attn_bwd_varlen(*bad) != 0
+    assert lib.attn_bwd_varlen_workspace_size(3, 4, 2, 0, 128) == 0
