@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8", "varlen_bf16"],
+                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8", "varlen_bf16",
+                             "varlen_fwdbwd_bf16"],
                     help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
                          "shape's forward with a 4096-key sliding window and ALiBi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,9 +369,11 @@ def bench_fp8(args):
     print(json.dumps(out), flush=True)
 
 
-def bench_varlen(args):
-    """Forward over 16 causal sequences packed without padding, lengths uniform in [128, 8192]
-    (seed 3), H=16, d=128, bf16: TFLOP/s with 4 d flops per query-key pair, halved for causal."""
+def bench_varlen(args, with_bwd=False):
+    """Forward (with_bwd: forward + backward) over 16 causal sequences packed without padding,
+    lengths uniform in [128, 8192] (seed 3), H=16, d=128, bf16: TFLOP/s with 4 d flops per
+    query-key pair for the forward and 10 d for the backward, halved for causal."""
+    import numpy as np
     import torch
 
     import exact_attention_online_amd as eao
@@ -390,27 +393,46 @@ def bench_varlen(args):
     T, ms_len = int(cu[-1]), int(lens.max())
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
+    if with_bwd:
+        g = np.random.Generator(np.random.PCG64(SEED + 1))
+        do = round_to(g.standard_normal(q.shape, dtype=np.float32), "bf16").to(dev).contiguous()
+        ws = torch.empty(eao.bwd_varlen_workspace_size(1 * len(lens), H, H, ms_len, d), dtype=torch.uint8,
+                         device=dev)
+        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
         eao.fwd_varlen(q, k, v, tcu, ms_len, True, None, o, lse)
+        if evs is not None:
+            evs[1].record()
+        if with_bwd:
+            eao.bwd_varlen(q, k, v, o, do, lse, tcu, ms_len, True, None, ws, dq, dk, dv)
+            if evs is not None:
+                evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        evs[i][0].record()
-        eao.fwd_varlen(q, k, v, tcu, ms_len, True, None, o, lse)
-        evs[i][1].record()
+        step(evs[i])
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
     ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    if not torch.isfinite(o).all():
+    ms_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if with_bwd else 0.0
+    if not torch.isfinite(o).all() or (with_bwd and not all(torch.isfinite(x).all() for x in (dq, dk, dv))):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
     flops = 4.0 * H * d * float((lens.astype(float) ** 2).sum()) / 2
+    total = flops * (3.5 if with_bwd else 1.0)
     out = {
-        "metric": "attention fwd TFLOPs/s over packed variable-length causal sequences",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "metric": ("attention fwd+bwd TFLOPs/s over packed variable-length causal sequences" if with_bwd else
+                   "attention fwd TFLOPs/s over packed variable-length causal sequences"),
+        "value": round(total / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -421,9 +443,10 @@ def bench_varlen(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"varlen_bf16: 16 sequences, lengths uniform in [128, 8192] (T={T}, longest {ms_len}), "
-                               f"H={H} d={d} causal fwd", "H": H, "d": d, "T": T, "lengths": lens.tolist(),
-                   "seed": SEED, "pass": "fwd"},
+        "config": {"workload": f"{args.workload}: 16 sequences, lengths uniform in [128, 8192] (T={T}, longest "
+                               f"{ms_len}), H={H} d={d} causal {'fwd+bwd' if with_bwd else 'fwd'}", "H": H, "d": d,
+                   "T": T, "lengths": lens.tolist(), "seed": SEED, "pass": "fwd+bwd" if with_bwd else "fwd"},
+        "kernel_ms": {"fwd_varlen": round(ms_call, 4), **({"bwd_varlen": round(ms_bwd, 4)} if with_bwd else {})},
         "roofline": {
             "kernel": "attn_fwd_kernel<bf16, d=128, causal, varlen>",
             "bound": "mfma",
@@ -445,8 +468,8 @@ def main():
               "the multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
 
-    if args.workload == "varlen_bf16":
-        bench_varlen(args)
+    if args.workload in ("varlen_bf16", "varlen_fwdbwd_bf16"):
+        bench_varlen(args, with_bwd=args.workload == "varlen_fwdbwd_bf16")
         return
     if args.workload == "fp8":
         bench_fp8(args)

@@ -269,8 +269,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // the heaviest workgroups of every head start first
   const int L = blockIdx.x;
   const int BHkv = gridDim.x / nkb;
-  const int kblk = L / BHkv;
-  const int bkv = L % BHkv;
+  // packed sequences: the same order, sequence by sequence (all blocks of sequence b's heads
+  // before sequence b + 1), so that the workgroups in flight share their sequence's query tiles
+  // in L2 as the workgroups of one batch do
+  const int kblk = VARLEN ? (L % (Hkv * nkb)) / Hkv : L / BHkv;
+  const int bkv = VARLEN ? (L / (Hkv * nkb)) * Hkv + L % Hkv : L % BHkv;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int k0 = kblk * kBwdKeys;
   const int kw = k0 + 32 * kq;                      // this wave's first key
@@ -579,8 +582,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  // packed sequences: the same order, sequence by sequence (see the dK/dV kernel)
+  const int Lb = VARLEN ? L % (Hq * nqb) : L;
+  const int BHo = VARLEN ? Hq : BH;
+  const int qblk = CAUSAL ? (nqb - 1 - Lb / BHo) : (Lb / BHo);
+  const int bh = VARLEN ? (L / (Hq * nqb)) * Hq + Lb % Hq : L % BH;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   const int bkv = b * Hkv + kvh;

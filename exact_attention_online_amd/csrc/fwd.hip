@@ -95,8 +95,13 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int G16 = lane >> 4, li = lane & 15;
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  // packed sequences: the same order sequence by sequence (all blocks of sequence b's heads
+  // before sequence b + 1), so that the workgroups in flight share their sequence's K/V tiles
+  // in L2 as the workgroups of one batch do
+  const int Lb = VARLEN ? L % (Hq * nqb) : L;
+  const int BHo = VARLEN ? Hq : BH;
+  const int qblk = CAUSAL ? (nqb - 1 - Lb / BHo) : (Lb / BHo);
+  const int bh = VARLEN ? (L / (Hq * nqb)) * Hq + Lb % Hq : L % BH;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   int N = N_in;
