@@ -582,11 +582,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int L = blockIdx.x;
-  // packed sequences: the same order, sequence by sequence (see the dK/dV kernel)
-  const int Lb = VARLEN ? L % (Hq * nqb) : L;
-  const int BHo = VARLEN ? Hq : BH;
-  const int qblk = CAUSAL ? (nqb - 1 - Lb / BHo) : (Lb / BHo);
-  const int bh = VARLEN ? (L / (Hq * nqb)) * Hq + Lb % Hq : L % BH;
+  // block order as in the forward: heads in chunks of HC (32 when that divides B * Hq; packed
+  // sequences: one sequence's heads), all query blocks of a chunk before the next, so that the
+  // workgroups in flight share their heads' K/V tiles in L2
+  const int HC = VARLEN ? Hq : ((BH % 32 == 0) ? 32 : BH);
+  const int Lb = L % (HC * nqb);
+  const int qblk = CAUSAL ? (nqb - 1 - Lb / HC) : (Lb / HC);
+  const int bh = (L / (HC * nqb)) * HC + Lb % HC;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   const int bkv = b * Hkv + kvh;

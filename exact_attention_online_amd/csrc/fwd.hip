@@ -95,13 +95,14 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int G16 = lane >> 4, li = lane & 15;
   const int L = blockIdx.x;
-  // packed sequences: the same order sequence by sequence (all blocks of sequence b's heads
-  // before sequence b + 1), so that the workgroups in flight share their sequence's K/V tiles
-  // in L2 as the workgroups of one batch do
-  const int Lb = VARLEN ? L % (Hq * nqb) : L;
-  const int BHo = VARLEN ? Hq : BH;
-  const int qblk = CAUSAL ? (nqb - 1 - Lb / BHo) : (Lb / BHo);
-  const int bh = VARLEN ? (L / (Hq * nqb)) * Hq + Lb % Hq : L % BH;
+  // Block order: the heads are taken in chunks of HC (32 when that divides B * Hq; packed
+  // sequences: one sequence's heads), all query blocks of a chunk before the next chunk, block
+  // by block across the chunk's heads (causal: longest blocks first).  The workgroups in flight
+  // then share their heads' K/V tiles in L2 instead of spreading over every head.
+  const int HC = VARLEN ? Hq : ((BH % 32 == 0) ? 32 : BH);
+  const int Lb = L % (HC * nqb);
+  const int qblk = CAUSAL ? (nqb - 1 - Lb / HC) : (Lb / HC);
+  const int bh = (L / (HC * nqb)) * HC + Lb % HC;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
   int N = N_in;
