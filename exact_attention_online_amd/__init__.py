@@ -12,11 +12,11 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
            "attn_status_string")
 
@@ -58,6 +58,8 @@ def load():
     lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 7 + [f, i, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_ext.restype = i
+    lib.attn_bwd_ext.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, vp, sz, vp]
+    lib.attn_bwd_ext.restype = i
     lib.attn_bwd_varlen_workspace_size.argtypes = [i] * 5
     lib.attn_bwd_varlen_workspace_size.restype = sz
     lib.attn_bwd_varlen.argtypes = [vp] * 10 + [i] * 7 + [f, i, vp, sz, vp]
@@ -244,6 +246,36 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_ext(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, window: int = 0, alibi_slopes=None,
+            workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of attn_fwd_ext (same window and ALiBi slopes); o, lse from fwd_ext."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    dt = _dtype_code(q)
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise AttnError("o and do must match q in shape, dtype and layout")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise AttnError("lse must be float32 [B,Hq,N]")
+    sl = None
+    if alibi_slopes is not None:
+        if (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq or not alibi_slopes.is_contiguous()
+                or alibi_slopes.device != q.device):
+            raise AttnError("alibi_slopes must be a contiguous float32 device tensor of Hq values")
+        sl = _ptr(alibi_slopes)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = bwd_workspace_size(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(load().attn_bwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                               _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, int(window), sl,
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
 

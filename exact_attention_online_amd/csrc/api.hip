@@ -21,6 +21,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
                          int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
                          const void* workspace, hipStream_t stream, int max_seqlen = 0, const int* cu = nullptr);
+hipError_t launch_bwd_dkdv_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                               void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale,
+                               bool bf16, const void* workspace, hipStream_t stream, int window, const float* slopes);
+hipError_t launch_bwd_dq_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                             void* dq, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                             const void* workspace, hipStream_t stream, int window, const float* slopes);
 hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                           int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
                           hipStream_t stream);
@@ -192,6 +198,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_ERR_HIP;
   if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s) !=
       hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                 int dtype, int window, const float* alibi_slopes, void* workspace, size_t workspace_bytes,
+                 attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
+                           workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (window < 0) return ATTN_ERR_INVALID;
+  if (alibi_slopes != nullptr && ((uintptr_t)alibi_slopes & 3u) != 0) return ATTN_ERR_INVALID;
+  const bool bf16 = dtype == ATTN_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (eao::launch_bwd_dkdv_ext(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16,
+                               workspace, s, window, alibi_slopes) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (eao::launch_bwd_dq_ext(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s,
+                             window, alibi_slopes) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

@@ -227,13 +227,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // ahead, each buffer a distinct LDS object); every operand read is a 16-byte row read.
 // VARLEN: packed sequences as in bwd_pre_kernel (K/V/dK/dV [Hkv,T,d], Q/dO [Hq,T,d]); a key block
 // past its sequence's end exits at once.
-template <bool BF16, int D, bool CAUSAL, bool VARLEN = false>
+// EXT: the sliding window and ALiBi bias of the forward with the same flag (key j visible to query
+// i only if i - j < window, and without the causal mask also j - i < window; score (i, j) of
+// query head h gets -slopes[h] |i - j| after the softmax scale).  The bias is constant in Q and
+// K, so the gradients keep their form and only the recomputed P changes: every query tile in
+// the band of the key block takes the masked path with the bias, tiles outside it are skipped.
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
-    float scale, const int* __restrict__ cu_seqlens) {
+    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = 8;                              // waves per workgroup
   constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
@@ -308,8 +313,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   const int nqb = (N + kBwdRows - 1) / kBwdRows;   // query tiles of the sequence
   const int nqb_ws = npad / kBwdRows;              // tiles per head in the workspace
-  const int qstart = CAUSAL ? (k0 / kBwdRows) : 0;
-  const int per_head = nqb - qstart;
+  // window (0: none; a window of N or more sees everything, so it is capped at N)
+  const int W = (EXT && window > 0) ? min(window, N) : 0;
+  // query tiles [qstart, qend) hold every row that sees a key of the block
+  int qstart = CAUSAL ? (k0 / kBwdRows) : 0;
+  int qend = nqb;
+  if (W > 0) {
+    if (!CAUSAL) qstart = max(0, k0 - W + 1) / kBwdRows;
+    qend = min(nqb, (k0 + kBwdKeys + W - 2) / kBwdRows + 1);
+  }
+  const int per_head = qend - qstart;
   const int total = G * per_head;
   // causal: only the first kBwdKeys / kBwdRows query blocks of every head cross the diagonal
   constexpr int kDiag = kBwdKeys / kBwdRows;
@@ -383,7 +396,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   // One query block (rows q0 ..) in buffer `par`; the next one is loaded meanwhile into the
   // other buffer.
-  auto step = [&](int q0, auto par, auto mask_tag) __attribute__((always_inline)) {
+  // ab2: the ALiBi slope of the block's query head in log2 units, negated (EXT only)
+  auto step = [&](int q0, float ab2, auto par, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     using Other = std::integral_constant<int, 1 - decltype(par)::value>;
     load_next(Other{});
@@ -414,9 +428,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rr + e;
-            float p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
-            if constexpr (MASK) {
-              if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
+            float p;
+            if constexpr (EXT) {
+              const int diff = q0 + 32 * qs + 8 * rr + 4 * g + e - key;   // query - key
+              p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, s[qs][r] * c - lv[e]));
+              const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
+              if (!vis) p = 0.f;
+            } else {
+              p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
+              if constexpr (MASK) {
+                if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
+              }
             }
             s[qs][r] = p;
           }
@@ -503,26 +525,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // unmasked steps [it, end) with the buffer parity of each step fixed at compile time
   auto run = [&](int end) __attribute__((always_inline)) {
     if ((it & 1) && it < end) {
-      step(0, Par1{}, std::false_type{});
+      step(0, 0.f, Par1{}, std::false_type{});
       ++it;
     }
     for (; it + 1 < end; it += 2) {
-      step(0, Par0{}, std::false_type{});
-      step(0, Par1{}, std::false_type{});
+      step(0, 0.f, Par0{}, std::false_type{});
+      step(0, 0.f, Par1{}, std::false_type{});
     }
     if (it < end) {
-      step(0, Par0{}, std::false_type{});
+      step(0, 0.f, Par0{}, std::false_type{});
       ++it;
     }
   };
-  if constexpr (CAUSAL) {
+  if constexpr (EXT) {
+    // every tile in the band takes the masked path (window edges and the bias vary per tile)
+    for (int hh = 0; hh < G; ++hh) {
+      const int base = hh * per_head;
+      const float ab2 = slopes != nullptr ? -slopes[kvh * G + hh] * kLog2e : 0.f;
+      for (; it < base + per_head; ++it) {
+        const int q0 = (qstart + it - base) * kBwdRows;
+        if (it & 1) step(q0, ab2, Par1{}, std::true_type{});
+        else step(q0, ab2, Par0{}, std::true_type{});
+      }
+    }
+  } else if constexpr (CAUSAL) {
     for (int hh = 0; hh < G; ++hh) {
       const int base = hh * per_head;
       const int diag_end = min(base + kDiag, base + per_head);
       for (; it < diag_end; ++it) {
         const int q0 = (qstart + it - base) * kBwdRows;
-        if (it & 1) step(q0, Par1{}, std::true_type{});
-        else step(q0, Par0{}, std::true_type{});
+        if (it & 1) step(q0, 0.f, Par1{}, std::true_type{});
+        else step(q0, 0.f, Par0{}, std::true_type{});
       }
       run(base + per_head);
     }
@@ -555,13 +588,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // chunks swizzled by swz) and K^T ([D][64] from the preprocess, chunk c of row r at
 // c ^ ((r / 2) % 8)).  All LDS reads are 16-byte rows.
 // VARLEN: packed sequences as in bwd_pre_kernel; a query block past its sequence's end exits at
-// once.
-template <bool BF16, int D, bool CAUSAL, bool VARLEN = false>
+// once.  EXT: window and ALiBi as in the dK/dV kernel; key tiles outside the block's band are
+// skipped and every other tile takes the masked path with the bias.
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
-    float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens) {
+    float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens, int window,
+    const float* __restrict__ slopes) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = kDqRows / 32;                  // waves per workgroup
   constexpr int TILE = kDqKeys * D;                 // 16-bit elements per tile
@@ -664,12 +699,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     }
   };
 
-  const int kend = CAUSAL ? min(N, q0 + kDqRows) : N;
+  // window (0: none; capped at N, which already sees everything) and ALiBi slope in log2 units
+  const int W = (EXT && window > 0) ? min(window, N) : 0;
+  const float ab2 = (EXT && slopes != nullptr) ? -slopes[h] * kLog2e : 0.f;
+  const int kend = CAUSAL ? min(N, q0 + kDqRows) : (W > 0 ? min(N, q0 + kDqRows + W - 1) : N);
   const int ntiles = (kend + kDqKeys - 1) / kDqKeys;
-  // a wave takes part in tiles [0, jact); under causal masking only tiles [jmask, jact) cross
-  // its diagonal
-  const int jact = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, (qw + 31) / kDqKeys + 1) : ntiles);
-  const int jmask = CAUSAL ? min(jact, q0 / kDqKeys) : jact;
+  // first tile with a key inside the window of the block's first row
+  const int jfirst = W > 0 ? max(0, q0 - W + 1) / kDqKeys : 0;
+  // a wave takes part in tiles [jfirst, jact); under causal masking only tiles [jmask, jact)
+  // cross its diagonal (EXT: every tile is masked)
+  const int jact = (qw >= N) ? 0
+                   : (CAUSAL ? min(ntiles, (qw + 31) / kDqKeys + 1)
+                             : (W > 0 ? min(ntiles, (qw + 31 + W - 1) / kDqKeys + 1) : ntiles));
+  const int jmask = EXT ? jfirst : (CAUSAL ? min(jact, q0 / kDqKeys) : jact);
 
   // S^T, dP^T for keys 32kb .. 32kb+31 of the tile in buffer `par`; lane owns query qrow,
   // register r holds key 32kb + 8(r/4) + 4g + r%4
@@ -692,9 +734,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
-      if constexpr (MASK) {
-        if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
+      float p;
+      if constexpr (EXT) {
+        const int diff = qrow - (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3));   // query - key
+        p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, st[r] * c - lse2));
+        const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
+        if (!vis) p = 0.f;
+      } else {
+        p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
+        if constexpr (MASK) {
+          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
+        }
       }
       st[r] = p * (dpt[r] + dd);
     }
@@ -764,10 +814,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  load_tiles(0, Par0{});
+  if (jfirst & 1) load_tiles(jfirst, Par1{});
+  else load_tiles(jfirst, Par0{});
   wait_all_loads();
   __syncthreads();
-  int j = 0;
+  int j = jfirst;
   auto run = [&](int end, auto mask_tag) __attribute__((always_inline)) {
     if ((j & 1) && j < end) {
       step(j, Par1{}, mask_tag);
@@ -822,33 +873,36 @@ static hipError_t launch_pre_t(const void* q, const void* k, const void* o, cons
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
 static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu,
-                                float scale, const void* workspace, hipStream_t stream) {
+                                float scale, const void* workspace, hipStream_t stream, int window = 0,
+                                const float* slopes = nullptr) {
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
   const int rows = VARLEN ? max_seqlen : N;
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
   const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
                      w.lse2, w.qt, w.dot, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e,
-                     scale, cu);
+                     scale, cu, window, slopes);
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
 static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               void* dq, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu, float scale,
-                              const void* workspace, hipStream_t stream) {
+                              const void* workspace, hipStream_t stream, int window = 0,
+                              const float* slopes = nullptr) {
   (void)lse;
   const int rows = VARLEN ? max_seqlen : N;
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
   const int nqb = (rows + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
-                     w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu);
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                     w.dsum, w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu,
+                     window, slopes);
   return hipGetLastError();
 }
 
@@ -900,6 +954,36 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     EAO_DISPATCH_V(launch_dq_t, true, q, k, v, dout, lse, dq, B, Hq, Hkv, N, max_seqlen, cu, scale, workspace, stream)
   }
   EAO_DISPATCH_V(launch_dq_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, cu, scale, workspace, stream)
+}
+// sliding window and/or ALiBi (dense layout): the dK/dV and dQ phases with EXT
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
+static hipError_t launch_dkdv_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                    void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                                    const void* workspace, hipStream_t stream, int window, const float* slopes) {
+  return launch_dkdv_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, nullptr, scale,
+                                                      workspace, stream, window, slopes);
+}
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
+static hipError_t launch_dq_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                  void* dq, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
+                                  hipStream_t stream, int window, const float* slopes) {
+  return launch_dq_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, nullptr, scale,
+                                                    workspace, stream, window, slopes);
+}
+
+hipError_t launch_bwd_dkdv_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                               void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale,
+                               bool bf16, const void* workspace, hipStream_t stream, int window,
+                               const float* slopes) {
+  EAO_DISPATCH_V(launch_dkdv_ext_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, scale, workspace, stream,
+                 window, slopes)
+}
+
+hipError_t launch_bwd_dq_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                             void* dq, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                             const void* workspace, hipStream_t stream, int window, const float* slopes) {
+  EAO_DISPATCH_V(launch_dq_ext_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, scale, workspace, stream, window,
+                 slopes)
 }
 #undef EAO_DISPATCH_V
 

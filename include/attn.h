@@ -100,6 +100,21 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     const int* cu_seqlens, int B, int Hq, int Hkv, int T, int max_seqlen, int d,
                     int causal, float softmax_scale, int dtype, attn_stream_t stream);
 
+/* Backward of attn_fwd_ext: gradients of L = <O, dO> with the sliding window and/or ALiBi bias
+ * of attn_fwd_ext ("FlashAttention-2: Faster Attention with Better Parallelism and Work
+ * Partitioning", OpenReview discussion, author responses: ALiBi and local attention;
+ * "FlashAttention (NeurIPS 2022)" notes, "Backward - Recomputation").  The bias does not depend
+ * on q or k, so the gradients keep the form of attn_bwd with P recomputed under the same mask
+ * and bias.  Arguments as for attn_bwd (same workspace size, attn_bwd_workspace_size), with
+ * o and lse from attn_fwd_ext and the same causal flag, scale, window and alibi_slopes.
+ * window 0 and NULL slopes give exactly attn_bwd's gradients up to rounding order.
+ * Returns an attn_status_t. */
+int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                 int d, int causal, float softmax_scale, int dtype, int window,
+                 const float* alibi_slopes, void* workspace, size_t workspace_bytes,
+                 attn_stream_t stream);
+
 /* Backward of attn_fwd_varlen: gradients of L = <O, dO> for variable-length sequences packed
  * without padding ("FlashAttention-2: Faster Attention with Better Parallelism and Work
  * Partitioning", OpenReview discussion, author responses: concatenated sequences and an array of

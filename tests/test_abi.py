@@ -165,3 +165,20 @@ def test_bwd_varlen_rejects_bad_arguments():
     bad = list(a); bad[12] = 3                                               # Hq % Hkv != 0
     assert lib.attn_bwd_varlen(*bad) != 0
     assert lib.attn_bwd_varlen_workspace_size(3, 4, 2, 0, 128) == 0
+
+
+def test_bwd_ext_rejects_bad_arguments():
+    lib = eao.load()
+    need = lib.attn_bwd_workspace_size(1, 2, 2, 100, 128)
+    # q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype, window, slopes, ws, bytes, stream
+    a = [P] * 9 + [1, 2, 2, 100, 128, 1, 0.1, 1, 4, NULL, P, need, NULL]
+    bad = list(a); bad[17] = -1                                              # negative window
+    assert lib.attn_bwd_ext(*bad) == 1
+    bad = list(a); bad[18] = ctypes.c_void_p(0x7F0000001002)                 # misaligned slopes
+    assert lib.attn_bwd_ext(*bad) == 1
+    bad = list(a); bad[16] = 2                                               # fp8
+    assert lib.attn_bwd_ext(*bad) == 2
+    bad = list(a); bad[13] = 96                                              # head dim
+    assert lib.attn_bwd_ext(*bad) == 2
+    bad = list(a); bad[20] = need - 1                                        # workspace too small
+    assert lib.attn_bwd_ext(*bad) == 3
