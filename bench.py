@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "fp8", "varlen_bf16",
+                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "window_alibi_fwdbwd_bf16", "fp8",
+                             "varlen_bf16",
                              "varlen_fwdbwd_bf16"],
                     help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
                          "shape's forward with a 4096-key sliding window and ALiBi")
@@ -217,9 +218,10 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
-def bench_window(args):
-    """Forward of the long shape (B=1, H=16, N=16384, d=128, bf16, causal) with a 4096-key sliding
-    window and ALiBi slopes 2^(-8 h / H): TFLOP/s over the visible query-key pairs."""
+def bench_window(args, with_bwd=False):
+    """Forward (with_bwd: forward + backward) of the long shape (B=1, H=16, N=16384, d=128, bf16,
+    causal) with a 4096-key sliding window and ALiBi slopes 2^(-8 h / H): TFLOP/s over the visible
+    query-key pairs (4 d flops per pair forward, 10 d backward)."""
     import numpy as np
     import torch
 
@@ -239,28 +241,46 @@ def bench_window(args):
     slopes = torch.tensor(2.0 ** (-8.0 * np.arange(1, w.Hq + 1) / w.Hq), dtype=torch.float32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
+    if with_bwd:
+        g = np.random.Generator(np.random.PCG64(SEED + 1))
+        do = round_to(g.standard_normal(tuple(q.shape), dtype=np.float32), w.dtype).to(dev).contiguous()
+        ws = torch.empty(eao.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
         eao.fwd_ext(q, k, v, True, w.scale, window, slopes, o, lse)
+        if evs is not None:
+            evs[1].record()
+        if with_bwd:
+            eao.bwd_ext(q, k, v, o, do, lse, True, w.scale, window, slopes, ws, dq, dk, dv)
+            if evs is not None:
+                evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        evs[i][0].record()
-        eao.fwd_ext(q, k, v, True, w.scale, window, slopes, o, lse)
-        evs[i][1].record()
+        step(evs[i])
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
     ms_call = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    if not torch.isfinite(o).all():
+    ms_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if with_bwd else 0.0
+    if not torch.isfinite(o).all() or (with_bwd and not all(torch.isfinite(x).all() for x in (dq, dk, dv))):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
     pairs = sum(min(i + 1, window) for i in range(w.N))          # visible (query, key) pairs per head
     flops = 4.0 * w.B * w.Hq * pairs * w.d
+    total = flops * (3.5 if with_bwd else 1.0)
     out = {
-        "metric": "attention fwd TFLOPs/s with a 4096-key sliding window and ALiBi (visible pairs)",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "metric": (f"attention {'fwd+bwd' if with_bwd else 'fwd'} TFLOPs/s with a 4096-key sliding window and "
+                   "ALiBi (visible pairs)"),
+        "value": round(total / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -271,9 +291,11 @@ def bench_window(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"window_alibi_bf16: B={w.B} H={w.Hq} N={w.N} d={w.d} causal, window {window}, "
-                               f"ALiBi slopes 2^(-8h/H), fwd", "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d,
-                   "window": window, "alibi": True, "seed": SEED, "pass": "fwd"},
+        "config": {"workload": f"{args.workload}: B={w.B} H={w.Hq} N={w.N} d={w.d} causal, window {window}, "
+                               f"ALiBi slopes 2^(-8h/H), {'fwd+bwd' if with_bwd else 'fwd'}", "B": w.B, "Hq": w.Hq,
+                   "N": w.N, "d": w.d, "window": window, "alibi": True, "seed": SEED,
+                   "pass": "fwd+bwd" if with_bwd else "fwd"},
+        "kernel_ms": {"fwd_ext": round(ms_call, 4), **({"bwd_ext": round(ms_bwd, 4)} if with_bwd else {})},
         "roofline": {
             "kernel": "attn_fwd_kernel<bf16, d=128, causal, window/ALiBi>",
             "bound": "mfma",
@@ -474,8 +496,8 @@ def main():
     if args.workload == "fp8":
         bench_fp8(args)
         return
-    if args.workload == "window_alibi_bf16":
-        bench_window(args)
+    if args.workload in ("window_alibi_bf16", "window_alibi_fwdbwd_bf16"):
+        bench_window(args, with_bwd=args.workload == "window_alibi_fwdbwd_bf16")
         return
     if args.workload != WORKLOAD:
         bench_decode(args)
