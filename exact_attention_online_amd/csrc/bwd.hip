@@ -397,8 +397,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // One query block (rows q0 ..) in buffer `par`; the next one is loaded meanwhile into the
   // other buffer.
   // ab2: the ALiBi slope of the block's query head in log2 units, negated (EXT only)
+  // mask_tag: 0 (or false) no mask; 1 (or true) masked (causal diagonal; EXT: window, causal and
+  // bias); 2 (EXT) bias only, for tiles wholly inside the band
   auto step = [&](int q0, float ab2, auto par, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int MODE = (int)decltype(mask_tag)::value;
+    constexpr bool MASK = MODE == 1;
     using Other = std::integral_constant<int, 1 - decltype(par)::value>;
     load_next(Other{});
     const short* qd = QD(par);
@@ -429,11 +432,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rr + e;
             float p;
-            if constexpr (EXT) {
+            if constexpr (EXT && MODE != 0) {
               const int diff = q0 + 32 * qs + 8 * rr + 4 * g + e - key;   // query - key
               p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, s[qs][r] * c - lv[e]));
-              const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
-              if (!vis) p = 0.f;
+              if constexpr (MASK) {
+                const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
+                if (!vis) p = 0.f;
+              }
+            } else if constexpr (EXT) {
+              p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
             } else {
               p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
               if constexpr (MASK) {
@@ -538,14 +545,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
   if constexpr (EXT) {
-    // every tile in the band takes the masked path (window edges and the bias vary per tile)
+    // tiles that cross a window edge or the causal diagonal take the masked path; tiles wholly
+    // inside the band take the bias-only path with ALiBi, the plain path without
+    using Mode0 = std::integral_constant<int, 0>;
+    using Mode1 = std::integral_constant<int, 1>;
+    using Mode2 = std::integral_constant<int, 2>;
+    const bool alibi = slopes != nullptr;
     for (int hh = 0; hh < G; ++hh) {
       const int base = hh * per_head;
-      const float ab2 = slopes != nullptr ? -slopes[kvh * G + hh] * kLog2e : 0.f;
+      const float ab2 = alibi ? -slopes[kvh * G + hh] * kLog2e : 0.f;
       for (; it < base + per_head; ++it) {
         const int q0 = (qstart + it - base) * kBwdRows;
-        if (it & 1) step(q0, ab2, Par1{}, std::true_type{});
-        else step(q0, ab2, Par0{}, std::true_type{});
+        const int dmin = q0 - (k0 + kBwdKeys - 1), dmax = q0 + kBwdRows - 1 - k0;   // query - key
+        const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
+        if (it & 1) {
+          if (!inside) step(q0, ab2, Par1{}, Mode1{});
+          else if (alibi) step(q0, ab2, Par1{}, Mode2{});
+          else step(q0, ab2, Par1{}, Mode0{});
+        } else {
+          if (!inside) step(q0, ab2, Par0{}, Mode1{});
+          else if (alibi) step(q0, ab2, Par0{}, Mode2{});
+          else step(q0, ab2, Par0{}, Mode0{});
+        }
       }
     }
   } else if constexpr (CAUSAL) {
@@ -729,17 +750,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     }
   };
   // dS^T = P^T (dP^T - D), packed as the B operand of dQ^T
+  // mask_tag as in the dK/dV kernel: 0 none, 1 masked, 2 (EXT) bias only
   auto p_ds = [&](int kt0, int kb, f32x16_t& st, const f32x16_t& dpt, i16x8_t (&sb)[2],
                   auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int MODE = (int)decltype(mask_tag)::value;
+    constexpr bool MASK = MODE == 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p;
-      if constexpr (EXT) {
+      if constexpr (EXT && MODE != 0) {
         const int diff = qrow - (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3));   // query - key
         p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, st[r] * c - lse2));
-        const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
-        if (!vis) p = 0.f;
+        if constexpr (MASK) {
+          const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
+          if (!vis) p = 0.f;
+        }
+      } else if constexpr (EXT) {
+        p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
       } else {
         p = __builtin_amdgcn_exp2f(st[r] * c - lse2);
         if constexpr (MASK) {
@@ -833,10 +860,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       ++j;
     }
   };
-  run(jmask, std::false_type{});
-  for (; j < jact; ++j) {
-    if (j & 1) step(j, Par1{}, std::true_type{});
-    else step(j, Par0{}, std::true_type{});
+  if constexpr (EXT) {
+    // tiles that cross a window edge or the diagonal for this wave's rows take the masked path,
+    // tiles wholly inside the band the bias-only (ALiBi) or plain path
+    using Mode0 = std::integral_constant<int, 0>;
+    using Mode1 = std::integral_constant<int, 1>;
+    using Mode2 = std::integral_constant<int, 2>;
+    const bool alibi = slopes != nullptr;
+    for (; j < jact; ++j) {
+      const int kt0 = j * kDqKeys;
+      const int dmin = qw - (kt0 + kDqKeys - 1), dmax = qw + 31 - kt0;   // query - key
+      const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
+      if (j & 1) {
+        if (!inside) step(j, Par1{}, Mode1{});
+        else if (alibi) step(j, Par1{}, Mode2{});
+        else step(j, Par1{}, Mode0{});
+      } else {
+        if (!inside) step(j, Par0{}, Mode1{});
+        else if (alibi) step(j, Par0{}, Mode2{});
+        else step(j, Par0{}, Mode0{});
+      }
+    }
+  } else {
+    run(jmask, std::false_type{});
+    for (; j < jact; ++j) {
+      if (j & 1) step(j, Par1{}, std::true_type{});
+      else step(j, Par0{}, std::true_type{});
+    }
   }
   for (; j < ntiles; ++j) idle(j);
 
