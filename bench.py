@@ -41,11 +41,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "decode_bf16", "decode4_bf16", "window_alibi_bf16", "window_alibi_fwdbwd_bf16", "fp8",
-                             "varlen_bf16",
-                             "varlen_fwdbwd_bf16"],
-                    help="the headline fwd+bwd workload (default), a split-KV decoding workload, or the long "
-                         "shape's forward with a 4096-key sliding window and ALiBi")
+                    choices=[WORKLOAD, "gqa_bf16", "ablation_bf16", "decode_bf16", "decode4_bf16", "window_alibi_bf16",
+                             "window_alibi_fwdbwd_bf16", "fp8", "varlen_bf16", "varlen_fwdbwd_bf16"],
+                    help="the headline fwd+bwd workload (default); the grouped-query fwd+bwd workload; the "
+                         "B=8 N=2048 forward, causal and not; split-KV decoding; the long shape with a 4096-key "
+                         "sliding window and ALiBi; fp8; packed variable-length sequences")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the warmup, run one plain device-to-device copy of MIB MiB (a kernel of "
                          "known traffic that scales HBM byte counters read under a profiler)")
@@ -89,7 +89,7 @@ def cpu_baseline(w, q, k, v, do, target_s):
         cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    f_head = 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
+    f_head = 4.0 * w.B * w.N * w.N * w.d / (2 if w.causal else 1)     # one query head, every batch entry
     G = w.Hq // w.Hkv
     t0 = time.perf_counter()
     heads = 0
@@ -106,8 +106,8 @@ def cpu_baseline(w, q, k, v, do, target_s):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"fp64 forward + backward of {heads} of {w.Hq} query heads (b=0) of the same "
-                  f"workload, {el:.1f} s; rate counted with the GPU's FLOP convention",
+        "sample": f"fp64 forward + backward of {heads} of {w.Hq} query heads (all {w.B} batch entries) of the "
+                  f"same workload, {el:.1f} s; rate counted with the GPU's FLOP convention",
     }
 
 
@@ -309,6 +309,85 @@ def bench_window(args, with_bwd=False):
     print(json.dumps(out), flush=True)
 
 
+def bench_ablation(args):
+    """Forward of the B=8, H=16, N=2048, d=128 bf16 shape, causal and non-causal (4 d flops per
+    query-key pair, halved for causal): value = both forwards' flops over both forwards' time."""
+    import torch
+
+    import exact_attention_online_amd as eao
+    from attn_inputs import WORKLOADS, draw, round_to
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    eao.load()
+    w = WORKLOADS["ablation_bf16"]
+    dev = torch.device("cuda:0")
+    _, q32, k32, v32, _ = draw(w.B, w.Hq, w.Hkv, w.N, w.d, SEED)
+    q, k, v = (round_to(x, w.dtype).to(dev).contiguous() for x in (q32, k32, v32))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    res = {}
+    # a call takes about 0.2 ms, comparable with the binding's per-call checks, so the timed loop
+    # calls the C ABI with the arguments marshalled once (the binding checked them in the warmup)
+    import ctypes
+
+    lib = eao.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for causal in (True, False):
+        for _ in range(args.warmup):
+            eao.fwd(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        call_args = (P(q), P(k), P(v), P(o), P(lse), w.B, w.Hq, w.Hkv, w.N, w.d, int(causal), w.scale, eao.BF16,
+                     None, None, None, stream)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            if lib.attn_fwd(*call_args) != 0:
+                print("attn_fwd failed", file=sys.stderr)
+                sys.exit(1)
+        t1.record()
+        torch.cuda.synchronize()
+        if not torch.isfinite(o).all():
+            print("non-finite output", file=sys.stderr)
+            sys.exit(1)
+        ms = t0.elapsed_time(t1) / args.steps
+        flops = 4.0 * w.B * w.Hq * w.N * w.N * w.d / (2 if causal else 1)
+        res["causal" if causal else "noncausal"] = (ms, flops)
+    tot_ms = sum(v[0] for v in res.values())
+    tot_f = sum(v[1] for v in res.values())
+    tf = {kk: v[1] / (v[0] * 1e-3) / 1e12 for kk, v in res.items()}
+    out = {
+        "metric": "attention fwd TFLOPs/s (bf16, B=8 H=16 N=2048 d=128, causal and non-causal)",
+        "value": round(tot_f / (tot_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tot_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"ablation_bf16: B={w.B} H={w.Hq} N={w.N} d={w.d} fwd, causal and non-causal",
+                   "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d, "seed": SEED, "pass": "fwd"},
+        "kernel_ms": {kk: round(v[0], 4) for kk, v in res.items()},
+        "kernel_tflops": {kk: round(v, 2) for kk, v in tf.items()},
+        "roofline": {
+            "kernel": "attn_fwd_kernel<bf16, d=128, causal and non-causal>",
+            "bound": "mfma",
+            "achieved": round(tot_f / (tot_ms * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_fp8(args):
     """FP8 forward (B=4, H=16, N=4096, d=128, non-causal, e4m3 with per-128-row scales): TFLOP/s of
     attn_fwd on prepared codes, against the dense fp8 MFMA peak; the preparation (Hadamard +
@@ -499,7 +578,10 @@ def main():
     if args.workload in ("window_alibi_bf16", "window_alibi_fwdbwd_bf16"):
         bench_window(args, with_bwd=args.workload == "window_alibi_fwdbwd_bf16")
         return
-    if args.workload != WORKLOAD:
+    if args.workload == "ablation_bf16":
+        bench_ablation(args)
+        return
+    if args.workload not in (WORKLOAD, "gqa_bf16"):
         bench_decode(args)
         return
 
@@ -512,7 +594,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     eao.load()
-    w = WORKLOADS[WORKLOAD]
+    wname = args.workload
+    w = WORKLOADS[wname]
     dev = torch.device("cuda:0")
     _, q32, k32, v32, do32 = draw(w.B, w.Hq, w.Hkv, w.N, w.d, SEED, with_grad=True)
     qc, kc, vc, doc = (round_to(x, w.dtype) for x in (q32, k32, v32, do32))
@@ -570,7 +653,7 @@ def main():
     # the dQ kernel three (S, dP, dQ: 1.5 x F_fwd), two of them recomputations
     dkdv_tflops = 2.0 * f_fwd / (dkdv_ms * 1e-3) / 1e12
     dq_tflops = 1.5 * f_fwd / (dq_ms * 1e-3) / 1e12
-    traffic = committed_traffic()
+    traffic = committed_traffic() if wname == WORKLOAD else None   # counters taken on the long workload
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -584,7 +667,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal fwd+bwd",
+        "config": {"workload": f"{wname}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal fwd+bwd",
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": w.causal,
                    "seed": SEED, "pass": "fwd+bwd"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
