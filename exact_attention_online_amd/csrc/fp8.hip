@@ -259,6 +259,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(m - muse);
       m = mnew;
+      // the probabilities come out pre-scaled by 2^8 (the exponent carries the + 8), so they
+      // convert to e4m3 as they are; l sums the same scaled values, which the final division
+      // cancels
+      const float muse8 = muse - 8.f;
       float rs = 0.f;
       int pw[8];
 #pragma unroll
@@ -268,18 +272,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
           float p[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(s[kb][r + e] * ceff - muse);
+            p[e] = __builtin_amdgcn_exp2f(s[kb][r + e] * ceff - muse8);
             rs += p[e];
           }
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
-          pw[(16 * kb + r) / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, wv, true);
+          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pw[(16 * kb + r) / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
         }
       l = l * alpha + rs;
-      // accumulator is kept in units of the current V block's scale
+      // accumulator is kept in units of the current V block's scale; the factor is exactly 1
+      // (and the multiplies are skipped) while neither the row maximum nor the V block changes
       const float rescale = alpha * (vs_cur / vs_new);
       vs_cur = vs_new;
+      if (__builtin_amdgcn_ballot_w64(rescale != 1.f) != 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= rescale;
+        for (int db = 0; db < 4; ++db) o[db] *= rescale;
+      }
       // B operand (P^T): slot e = 16kb + r  ->  key 32kb + 16(r/8) + 8g + (r%8)
       const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
@@ -302,8 +309,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     __syncthreads();
   }
 
-  const float lt = sum_halves(l);
-  const float fin = vs_cur * (1.f / 256.f) / lt;
+  const float lt = sum_halves(l);                // 2^8 times the sum of the probabilities
+  const float fin = vs_cur / lt;
   if (qrow < N) {
     uint16_t* Op = O + q_off + (size_t)qrow * D;
 #pragma unroll
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         pk.y = pack2<true>(o[db][4 * rr + 2] * fin, o[db][4 * rr + 3] * fin);
         *(uint2*)(Op + d0) = pk;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
+    if (g == 0) LSE[(size_t)bh * N + qrow] = (m - 8.f + __log2f(lt)) * kLn2;
   }
 }
 
