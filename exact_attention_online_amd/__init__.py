@@ -104,6 +104,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _req(device, **named):
+    """Every tensor the library will dereference: contiguous, on `device`, and (where given) of
+    the expected shape and dtype.  name=(tensor, shape or None, dtype or None).  A host tensor
+    here would reach a kernel as a host address, so it is rejected before any call."""
+    for name, (t, shape, dtype) in named.items():
+        if not t.is_cuda or t.device != device or not t.is_contiguous():
+            raise AttnError(f"{name} must be a contiguous tensor on {device}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise AttnError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise AttnError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _shapes(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise AttnError(f"expected q [B,Hq,N,d], k/v [B,Hkv,N,d]; got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
@@ -130,6 +143,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _req(q.device, out=(out, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32))
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, dt, None, None, None, _stream(q.device)))
     return out, lse
@@ -154,6 +168,7 @@ def fwd_ext(q, k, v, causal: bool = False, scale: float | None = None, window: i
                 or alibi_slopes.device != q.device):
             raise AttnError("alibi_slopes must be a contiguous float32 device tensor of Hq values")
         sl = _ptr(alibi_slopes)
+    _req(q.device, out=(out, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32))
     _check(load().attn_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
                                int(bool(causal)), scale, dt, int(window), sl, _stream(q.device)))
     return out, lse
@@ -182,6 +197,8 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _req(q.device, out=(out, q.shape, q.dtype), lse=(lse, (Hq, T), torch.float32),
+         cu_seqlens=(cu_seqlens, (B + 1,), torch.int32))
     _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens.contiguous()), B,
                                   Hq, Hkv, T, int(max_seqlen), d, int(bool(causal)), scale, dt, _stream(q.device)))
     return out, lse
@@ -214,6 +231,8 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     need = splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _req(q.device, out=(out, q.shape, q.dtype), lse=(lse, (B, Hq, Nq), torch.float32),
+         workspace=(workspace, None, None))
     wsb = workspace.numel() * workspace.element_size()
     _check(load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                                    int(bool(causal)), scale, dt, int(num_splits), _ptr(workspace), wsb,
@@ -243,6 +262,9 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
+         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
+         dv=(dv, v.shape, v.dtype))
     _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q.device)))
@@ -273,6 +295,9 @@ def bwd_ext(q, k, v, o, do, lse, causal: bool = False, scale: float | None = Non
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
+         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
+         dv=(dv, v.shape, v.dtype))
     _check(load().attn_bwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, int(window), sl,
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
@@ -314,6 +339,9 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, causal: bool = 
     dq = torch.zeros_like(q) if dq is None else dq
     dk = torch.zeros_like(k) if dk is None else dk
     dv = torch.zeros_like(v) if dv is None else dv
+    _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (Hq, T), torch.float32),
+         cu_seqlens=(cu_seqlens, (B + 1,), torch.int32), workspace=(workspace, None, None),
+         dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype), dv=(dv, v.shape, v.dtype))
     _check(load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                   _ptr(dv), _ptr(cu_seqlens.contiguous()), B, Hq, Hkv, T, int(max_seqlen), d,
                                   int(bool(causal)), scale, dt, _ptr(workspace),
@@ -324,8 +352,12 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, causal: bool = 
 def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, between=None):
     """attn_bwd as its three phases (preprocess, dK/dV, dQ); ``between(i)`` (if given) is called
     before phase i = 0, 1, 2 and after the last one with i = 3, e.g. to record stream events."""
+    torch = _torch()
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     dt = _dtype_code(q)
+    _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
+         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
+         dv=(dv, v.shape, v.dtype))
     lib, st = load(), _stream(q.device)
     wsb = workspace.numel() * workspace.element_size()
     hook = between or (lambda i: None)
@@ -357,7 +389,9 @@ def fp8_prep(x, signs=None, out=None, descale=None):
     if signs is not None:
         if signs.dtype != torch.int8 or signs.numel() != d or not signs.is_cuda:
             raise AttnError("signs must be an int8 device tensor of length d")
+        _req(x.device, signs=(signs, (d,), torch.int8))
         sp = _ptr(signs)
+    _req(x.device, out=(out, x.shape, torch.uint8), descale=(descale, (B, H, (N + 127) // 128), torch.float32))
     _check(load().attn_fp8_prep(_ptr(x), _ptr(out), _ptr(descale), sp, B, H, N, d, _stream(x.device)))
     return out, descale
 
@@ -379,6 +413,9 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool = False, s
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    _req(q8.device, q_descale=(q_descale, (B, Hq, nb), torch.float32), k_descale=(k_descale, (B, Hkv, nb), torch.float32),
+         v_descale=(v_descale, (B, Hkv, nb), torch.float32), out=(out, q8.shape, torch.bfloat16),
+         lse=(lse, (B, Hq, N), torch.float32))
     _check(load().attn_fwd(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, FP8_E4M3, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _stream(q8.device)))
     return out, lse

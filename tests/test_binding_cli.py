@@ -1,0 +1,57 @@
+"""Host-side behaviour without a GPU: the binding refuses to run without the built library and
+rejects host tensors before any library call; bench.py refuses more than one GPU and fails
+loudly (no CPU fallback) where no GPU is visible."""
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import exact_attention_online_amd as eao
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_missing_library_raises(monkeypatch):
+    monkeypatch.setattr(eao, "_lib", None)
+    monkeypatch.setattr(eao, "library_path", lambda: os.path.join(ROOT, "no-such-dir", "libattn.so"))
+    with pytest.raises(eao.AttnError, match="missing"):
+        eao.load()
+
+
+def test_host_tensors_are_rejected_before_any_call(monkeypatch):
+    # a library stand-in that fails the test if anything reaches it
+    class Trap:
+        def __getattr__(self, name):
+            raise AssertionError(f"library function {name} reached with host tensors")
+
+    monkeypatch.setattr(eao, "_lib", Trap())
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(eao.AttnError, match="device"):
+        eao.fwd(q, q, q)
+    with pytest.raises(eao.AttnError):
+        eao.bwd(q, q, q, q, q, torch.zeros(1, 2, 8))
+    with pytest.raises(eao.AttnError):
+        eao.fwd_varlen(q[0], q[0], q[0], torch.tensor([0, 8], dtype=torch.int32), 8)
+    with pytest.raises(eao.AttnError):
+        eao.fp8_prep(torch.zeros(1, 2, 8, 128))
+
+
+def _bench(*args, env=None):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=300, env=env, cwd=ROOT)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour where no GPU is visible")
+def test_bench_fails_loudly_without_a_gpu():
+    r = _bench("--steps", "1", "--warmup", "0", "--no-cpu-baseline")
+    assert r.returncode != 0
+    assert "no GPU visible" in r.stderr
+    assert '"value"' not in r.stdout
