@@ -9,7 +9,7 @@
 //
 // Three kernels on the caller's stream, none of them atomic:
 //   1. bwd_pre: per query row -D = -rowsum(dO * O) and LSE * log2(e), and the 64-row tiles of
-//      Q and dO written transposed ([d][64 rows], see the workspace layout below), all in the
+//      Q, dO and K written transposed ([d][64 rows], see the workspace layout below), all in the
 //      caller's workspace.
 //   2. bwd_dkdv: one workgroup of 8 waves per (batch, K/V head, block of 128 keys), in two
 //      roles over the same four quarters of 32 keys (one wave of each role per SIMD).  A "P
@@ -26,18 +26,23 @@
 //      with Q, dO read as rows of the row-major tiles and dO^T, Q^T as rows of the transposed
 //      tiles (all ds_read_b128).  Two contractions per wave keep each wave under 256
 //      registers, so two waves share a SIMD and one's vector work overlaps the other's MFMAs.
-//   3. bwd_dq: one workgroup per (batch, query head, block of 128 query rows), shaped like the
-//      forward: a lane owns one query row, so LSE and D are one register each.  Per key tile:
+//   3. bwd_dq: one workgroup of 8 waves per (batch, query head, block of 256 query rows),
+//      shaped like the forward: a lane owns one query row, so LSE and D are one register each.
+//      Per key tile of 64:
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T,
 //      with dS^T fed from the accumulator into the last MFMA (k relabelled as in the forward)
-//      and K^T read through ds_read_b64_tr_b16; dQ = scale * dQ^T is written once at the end.
+//      and K^T read as rows of the transposed tiles from bwd_pre; dQ = scale * dQ^T is written
+//      once at the end.
 // Splitting dQ off costs two extra contractions (S and dP are recomputed) but replaces the
 // fp32 atomic accumulation of dQ, whose ordered completion stalled the loads of the
 // key-stationary kernel, with plain register accumulation.
 //
 // Keys or query rows past N read as zeros (bounds-checked buffer loads).  Zero K/V rows and
 // zero Q/dO/D rows make every contribution that crosses the end of the sequence vanish exactly,
-// so only the causal diagonal is masked.
+// so only the causal diagonal (and, with a sliding window, the band's edges) is masked.
+//
+// Variants of the same kernels: VARLEN (sequences packed without padding, offsets from
+// cu_seqlens) and EXT (sliding window and ALiBi bias), described at the kernels.
 #include <type_traits>
 
 #include "common.hpp"
