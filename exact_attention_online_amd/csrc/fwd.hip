@@ -12,8 +12,9 @@
 //     the NWV waves each own QB * 32 query rows.  The plain forward runs 8 waves (256 rows,
 //     one workgroup and two waves per SIMD on a CU), so each K/V tile loaded into LDS serves
 //     256 query rows; the variants with window/ALiBi (more registers) and variable lengths
-//     (finer early exit) run 4.  Causal launches visit the longest query blocks first (block
-//     ids count down), so short blocks fill the tail of the schedule.
+//     (finer early exit) run 4.  The heads are taken in chunks (32 heads, or one packed
+//     sequence's heads) so that the workgroups in flight share K/V tiles in L2; within a chunk,
+//     causal launches visit the longest query blocks first, so short blocks fill the tail.
 //   * transposed formulation: each wave computes S^T = K Q^T and O^T = V^T P^T with
 //     v_mfma_f32_32x32x16.  In the S^T accumulator a lane owns one query (column l % 32) and 16
 //     keys, so the row maximum and row sum are lane-local; one v_permlane32_swap combines the
