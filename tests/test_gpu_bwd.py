@@ -136,3 +136,21 @@ def test_workspace_contents_do_not_matter():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert _err(x, f64(y)) <= 1e-2
+
+
+@pytest.mark.parametrize("kind", ["up", "down", "spike"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_running_maximum_growth(kind, dtype, causal):
+    # inputs of test_gpu_fwd's running-maximum test (scores up to about 100); the gradients scale
+    # with |K| and |Q| (about 30-40 along one direction), so the bar is the unit-normal one
+    # relative to max(1, max |reference|)
+    from test_gpu_fwd import _ramp_inputs
+
+    q, k, v = _ramp_inputs(kind, 515, 128, dtype, seed=12)
+    g = np.random.Generator(np.random.PCG64(13))
+    do = round_to(g.standard_normal(q.shape, dtype=np.float32), dtype)
+    dq, dk, dv = _gpu_grads(q, k, v, do, causal)
+    refs = A.backward(q, k, v, do, causal, 1.0 / np.sqrt(128))
+    for got, ref in zip((dq, dk, dv), refs):
+        assert _err(got, ref) <= TOL[dtype] * max(1.0, np.abs(ref).max())

@@ -140,3 +140,34 @@ def test_custom_scale():
     ro, rlse = A.forward(q, k, v, False, 0.05)
     assert np.abs(f64(o) - ro).max() <= TOL_O["fp16"]
     assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+
+
+# ---------------------------------------------------------------- running-maximum growth
+def _ramp_inputs(kind, N, d, dtype, seed):
+    """Q rows and K rows along one direction u with key weights that ramp up ('up': the running
+    maximum grows by far more than 2^8 from tile to tile, so the rescale of the accumulator runs
+    on every tile), ramp down ('down': the first tile holds the maximum) or stay small but for one
+    late key ('spike': one jump).  Scores reach about 100 (natural units)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    t = np.arange(N) / max(N - 1, 1)
+    alpha = {"up": 38.0 * t, "down": 38.0 * (1.0 - t), "spike": np.where(np.arange(N) == (7 * N) // 8, 38.0, 1.0)}[kind]
+    q = (30.0 * u)[None, :] + 0.3 * g.standard_normal((N, d))
+    k = alpha[:, None] * u[None, :] + 0.3 * g.standard_normal((N, d))
+    v = g.standard_normal((N, d))
+    shape = (1, 1, N, d)
+    return tuple(round_to(x.reshape(shape).astype(np.float32), dtype) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("kind", ["up", "down", "spike"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_running_maximum_growth(kind, dtype, causal):
+    # O here is a sharp average of a few V rows (|O| up to max |V|, about 3.5, against ~0.05 for
+    # unit-normal inputs), so the bar is the unit-normal one relative to max(1, max |O|)
+    q, k, v = _ramp_inputs(kind, 515, 128, dtype, seed=11)
+    o, lse = _run(q, k, v, causal)
+    ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(128))
+    assert np.abs(f64(o) - ro).max() <= TOL_O[dtype] * max(1.0, np.abs(ro).max())
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
