@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "attention", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
@@ -419,3 +419,31 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool = False, s
     _check(load().attn_fwd(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, FP8_E4M3, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _stream(q8.device)))
     return out, lse
+
+
+_AttentionFn = None
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Differentiable attention for fp16/bf16 q [B,Hq,N,d], k/v [B,Hkv,N,d] on one device: the
+    forward is attn_fwd (O and the logsumexp saved), the backward attn_bwd (probabilities
+    recomputed); dK/dV are summed over each query-head group.  Gradients flow to q, k and v."""
+    global _AttentionFn
+    torch = _torch()
+    if _AttentionFn is None:
+        class _Fn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q_, k_, v_, causal_, scale_):
+                o, lse = fwd(q_, k_, v_, causal=causal_, scale=scale_)
+                ctx.save_for_backward(q_, k_, v_, o, lse)
+                ctx.causal, ctx.scale = causal_, scale_
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q_, k_, v_, o, lse = ctx.saved_tensors
+                dq, dk, dv = bwd(q_, k_, v_, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale)
+                return dq, dk, dv, None, None
+
+        _AttentionFn = _Fn
+    return _AttentionFn.apply(q, k, v, bool(causal), scale)
