@@ -184,6 +184,25 @@ def bench_decode(args):
     if not torch.isfinite(o).all():
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
+    # the same call captured once in a HIP graph and replayed back to back, as a decoding loop
+    # would launch it: no Python or launch gaps between the steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / steps
     kv_bytes = 2.0 * w.B * w.Hkv * w.Nk * w.d * 2
     algo = kv_bytes + 2.0 * (2 * w.B * w.Hq * w.Nq * w.d) + 4.0 * w.B * w.Hq * w.Nq   # + Q read, O written, LSE
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -213,6 +232,8 @@ def bench_decode(args):
             "traffic": None,
         },
     }
+    out["graph_replay"] = {"ms_per_step": round(ms_graph, 5), "value": round(kv_bytes / (ms_graph * 1e-3) / 1e9, 1),
+                           "unit": "GB/s"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, qc, kc, vc, args.cpu_seconds)
     print(json.dumps(out), flush=True)
