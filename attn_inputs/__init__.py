@@ -17,7 +17,10 @@ Recipe (applies to every workload):
   * fp8 extras (drawn after dO would be, from the same generator): for each of Q, K, V in that
     order, ``round(0.001 * numel)`` distinct flat indices chosen uniformly without replacement,
     whose entries are multiplied by 10 (outliers); then one sign vector of length d with entries
-    +-1 (the random signs of the incoherent-processing transform).
+    +-1 (the random signs of the incoherent-processing transform);
+  * tensors too large to draw on the host (``draw_on_device``): torch's generator on the device,
+    seeded, ``randn`` in float32, then rounded like the rest; the oracle gets copies of the heads
+    it checks.
 """
 from __future__ import annotations
 
@@ -26,7 +29,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "DECODE_WORKLOADS", "DecodeWorkload", "draw", "draw_decode", "draw_fp8",
-           "draw_varlen", "varlen_lengths", "round_to", "DTYPES"]
+           "draw_on_device", "draw_varlen", "varlen_lengths", "round_to", "DTYPES"]
 
 DTYPES = ("fp16", "bf16")
 
@@ -168,4 +171,18 @@ def workload_inputs(w: Workload, seed: int):
     out = {"q": round_to(q, w.dtype), "k": round_to(k, w.dtype), "v": round_to(v, w.dtype)}
     if do is not None:
         out["do"] = round_to(do, w.dtype)
+    return out
+
+
+def draw_on_device(shapes, dtype: str, seed: int, device):
+    """One N(0,1) tensor per shape in ``shapes``, drawn in that order on ``device`` by torch's
+    generator seeded with ``seed`` (float32, then rounded to fp16/bf16 as in round_to)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    out = []
+    for shape in shapes:
+        out.append(torch.randn(shape, generator=gen, dtype=torch.float32, device=device).to(tdt))
     return out
