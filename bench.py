@@ -332,7 +332,8 @@ def bench_window(args, with_bwd=False):
 
 def bench_ablation(args):
     """Forward of the B=8, H=16, N=2048, d=128 bf16 shape, causal and non-causal (4 d flops per
-    query-key pair, halved for causal): value = both forwards' flops over both forwards' time."""
+    query-key pair, halved for causal): value = both forwards' flops over both forwards' time.
+    The small batch x heads setting (B=1, causal) is reported beside it as `small_batch`."""
     import torch
 
     import exact_attention_online_amd as eao
@@ -379,6 +380,29 @@ def bench_ablation(args):
     tot_ms = sum(v[0] for v in res.values())
     tot_f = sum(v[1] for v in res.values())
     tf = {kk: v[1] / (v[0] * 1e-3) / 1e12 for kk, v in res.items()}
+    # the pages' second ablation setting, small batch x heads (B=1, H=16, same N, d, causal),
+    # timed the same way beside the first; not part of value
+    _, s32, t32, u32, _ = draw(1, w.Hq, w.Hkv, w.N, w.d, SEED)
+    sq, sk, sv = (round_to(x, w.dtype).to(dev).contiguous() for x in (s32, t32, u32))
+    so = torch.empty_like(sq)
+    slse = torch.empty((1, w.Hq, w.N), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        eao.fwd(sq, sk, sv, causal=True, scale=w.scale, out=so, lse=slse)
+    small_args = (P(sq), P(sk), P(sv), P(so), P(slse), 1, w.Hq, w.Hkv, w.N, w.d, 1, w.scale, eao.BF16, None, None,
+                  None, stream)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        if lib.attn_fwd(*small_args) != 0:
+            print("attn_fwd failed", file=sys.stderr)
+            sys.exit(1)
+    t1.record()
+    torch.cuda.synchronize()
+    if not torch.isfinite(so).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+    small_ms = t0.elapsed_time(t1) / args.steps
+    small_tf = 4.0 * w.Hq * w.N * w.N * w.d / 2 / (small_ms * 1e-3) / 1e12
     out = {
         "metric": "attention fwd TFLOPs/s (bf16, B=8 H=16 N=2048 d=128, causal and non-causal)",
         "value": round(tot_f / (tot_ms * 1e-3) / 1e12, 2),
@@ -396,6 +420,8 @@ def bench_ablation(args):
                    "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d, "seed": SEED, "pass": "fwd"},
         "kernel_ms": {kk: round(v[0], 4) for kk, v in res.items()},
         "kernel_tflops": {kk: round(v, 2) for kk, v in tf.items()},
+        "small_batch": {"config": f"B=1 H={w.Hq} N={w.N} d={w.d} causal fwd", "ms": round(small_ms, 4),
+                        "tflops": round(small_tf, 2)},
         "roofline": {
             "kernel": "attn_fwd_kernel<bf16, d=128, causal and non-causal>",
             "bound": "mfma",

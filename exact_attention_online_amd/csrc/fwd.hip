@@ -11,8 +11,10 @@
 //   * grid: one workgroup per (batch, query head, block of BR = NWV * QB * 32 query rows);
 //     the NWV waves each own QB * 32 query rows.  The plain forward runs 8 waves (256 rows,
 //     one workgroup and two waves per SIMD on a CU), so each K/V tile loaded into LDS serves
-//     256 query rows; the variants with window/ALiBi (more registers) and variable lengths
-//     (finer early exit) run 4.  The heads are taken in chunks (32 heads, or one packed
+//     256 query rows, unless 256-row blocks would give the 256 CUs fewer than two workgroups
+//     each (few batches x heads x rows): then 4 waves (128 rows, twice the workgroups), which
+//     fills the idle CUs; each row's arithmetic is the same either way.  The variants with
+//     window/ALiBi (more registers) and variable lengths (finer early exit) run 4.  The heads are taken in chunks (32 heads, or one packed
 //     sequence's heads) so that the workgroups in flight share K/V tiles in L2; within a chunk,
 //     causal launches visit the longest query blocks first, so short blocks fill the tail.
 //   * transposed formulation: each wave computes S^T = K Q^T and O^T = V^T P^T with
@@ -435,10 +437,12 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   }
 }
 
-template <bool BF16, int D, int QB, int BC, bool CAUSAL>
-static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                               int Hkv, int N, float scale, hipStream_t stream) {
-  constexpr int NWV = 8;
+// compute units of an MI355X (gfx950)
+constexpr int kNumCUs = 256;
+
+template <bool BF16, int D, int QB, int BC, bool CAUSAL, int NWV>
+static hipError_t launch_fwd_nwv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                 int Hkv, int N, float scale, hipStream_t stream) {
   constexpr int BR = NWV * QB * 32;
   const int nqb = (N + BR - 1) / BR;
   const int BH = B * Hq;
@@ -447,6 +451,16 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
                      (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e, 0,
                      (const float*)nullptr, 1.f, (const int*)nullptr);
   return hipGetLastError();
+}
+
+// 256-row blocks when they give every CU at least two workgroups, else 128-row blocks
+template <bool BF16, int D, int QB, int BC, bool CAUSAL>
+static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int N, float scale, hipStream_t stream) {
+  const long long blocks8 = (long long)B * Hq * ((N + 8 * QB * 32 - 1) / (8 * QB * 32));
+  if (blocks8 < 2 * kNumCUs)
+    return launch_fwd_nwv<BF16, D, QB, BC, CAUSAL, 4>(q, k, v, o, lse, B, Hq, Hkv, N, scale, stream);
+  return launch_fwd_nwv<BF16, D, QB, BC, CAUSAL, 8>(q, k, v, o, lse, B, Hq, Hkv, N, scale, stream);
 }
 
 template <bool BF16, int D, bool CAUSAL>

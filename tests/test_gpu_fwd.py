@@ -171,3 +171,38 @@ def test_forward_running_maximum_growth(kind, dtype, causal):
     ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(128))
     assert np.abs(f64(o) - ro).max() <= TOL_O[dtype] * max(1.0, np.abs(ro).max())
     assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+
+
+# ---------------------------------------------------------------- block size chosen by grid size
+# 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512, else 128-row blocks (4 waves).  Below:
+# 2*64*ceil(1100/256) = 640 blocks, so the 8-wave path, over every output with a ragged tail
+# (1100 = 4*256 + 76); one head alone (1*1*5 blocks) takes the 4-wave path, and each row's
+# arithmetic is the same in both, so the two agree bit for bit.
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_full_and_block_size_invariance(dtype, d, causal):
+    B, Hq, Hkv, N = 2, 64, 16, 1100
+    assert B * Hq * ((N + 255) // 256) >= 512
+    q, k, v = _inputs(B, Hq, Hkv, N, d, dtype, seed=20 + d + causal)
+    o, lse = _run(q, k, v, causal)
+    ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(d))
+    assert np.abs(f64(o) - ro).max() <= TOL_O[dtype]
+    assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
+    G = Hq // Hkv
+    for b, h in ((0, 0), (1, 37), (1, 63)):
+        g = h // G
+        o1, l1 = _run(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], causal)
+        assert torch.equal(o1[0, 0].cpu(), o[b, h].cpu()), (b, h)
+        assert torch.equal(l1[0, 0].cpu(), lse[b, h].cpu()), (b, h)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_batch_heads_workload_sampled(causal):
+    # B=1, H=16, N=2048, d=128: 128 blocks of 256 rows, so the 4-wave path with 256 blocks
+    q, k, v = _inputs(1, 16, 16, 2048, 128, "bf16", seed=21 + causal)
+    o, lse = _run(q, k, v, causal)
+    rows = sample_rows(2048, seed=21)
+    for h in (0, 7, 15):
+        ro, rlse = A.forward_rows(q, k, v, causal, 1.0 / np.sqrt(128), 0, h, rows)
+        assert np.abs(f64(o)[0, h, rows] - ro).max() <= TOL_O["bf16"], h
+        assert np.abs(f64(lse)[0, h, rows] - rlse).max() <= TOL_LSE, h
