@@ -51,7 +51,7 @@ namespace eao {
 
 constexpr int kBwdKeys = 128;   // keys per dK/dV workgroup (32 per wave)
 constexpr int kBwdRows = 64;    // query rows per dK/dV step (one tile)
-constexpr int kDqRows = 256;    // query rows per dQ workgroup (8 waves x 32)
+constexpr int kDqRows = 256;    // query rows per dQ workgroup (8 waves x 32; 4 x 32 on small grids)
 constexpr int kDqKeys = 64;     // keys per dQ step
 
 // Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256),
@@ -609,22 +609,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------ 3. dQ
 // One workgroup of 8 waves per (batch, query head, block of 256 query rows); a wave owns 32
-// rows (two waves per SIMD).  Per key tile of 64, three tiles in double-buffered LDS, each pair
-// of buffers distinct LDS objects, filled by direct buffer -> LDS loads: [K | V] ([64][D],
+// rows (two waves per SIMD).  When 256-row blocks would give the CUs fewer than two workgroups
+// each (dense layout, no window or bias), 4 waves and 128 rows, twice the workgroups; a row's
+// arithmetic is the same either way.  Per key tile of 64, three tiles in double-buffered LDS,
+// each pair of buffers distinct LDS objects, filled by direct buffer -> LDS loads: [K | V] ([64][D],
 // chunks swizzled by swz) and K^T ([D][64] from the preprocess, chunk c of row r at
 // c ^ ((r / 2) % 8)).  All LDS reads are 16-byte rows.
 // VARLEN: packed sequences as in bwd_pre_kernel; a query block past its sequence's end exits at
 // once.  EXT: window and ALiBi as in the dK/dV kernel; key tiles outside the block's band are
 // skipped and every other tile takes the masked path with the bias.
-template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, int ROWS = kDqRows>
+__global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
     float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens, int window,
     const float* __restrict__ slopes) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
-  constexpr int NW = kDqRows / 32;                  // waves per workgroup
+  constexpr int NW = ROWS / 32;                     // waves per workgroup
   constexpr int TILE = kDqKeys * D;                 // 16-bit elements per tile
   constexpr int PIECES = TILE * 2 / 1024;           // 1 KB direct-load pieces per tile
   static_assert(PIECES % NW == 0, "each wave moves the same number of pieces");
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   size_t kv_off = (size_t)bkv * N_in * D;
   if constexpr (VARLEN) {
     const SeqRange sr = seq_range(cu_seqlens, b, N_in, npad);
-    if (qblk * kDqRows >= sr.n) return;              // the whole workgroup: no barrier reached
+    if (qblk * ROWS >= sr.n) return;                 // the whole workgroup: no barrier reached
     N = sr.n;
     q_row0 = (size_t)h * N_in + sr.s0;
     kv_off = ((size_t)kvh * N_in + sr.s0) * D;
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int ntile_all = npad / kDqKeys;
   const __amdgpu_buffer_rsrc_t trs = make_rsrc(KT + (size_t)bkv * ntile_all * TILE, (uint32_t)ntile_all * TILE * 2);
 
-  const int q0 = qblk * kDqRows;
+  const int q0 = qblk * ROWS;
   const int qw = q0 + 32 * w;
   const int qrow = qw + l32;
   // B operands for S^T = K Q^T and dP^T = V dO^T: lane holds row qrow, 8 columns 16kk + 8g
@@ -728,7 +730,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   // window (0: none; capped at N, which already sees everything) and ALiBi slope in log2 units
   const int W = (EXT && window > 0) ? min(window, N) : 0;
   const float ab2 = (EXT && slopes != nullptr) ? -slopes[h] * kLog2e : 0.f;
-  const int kend = CAUSAL ? min(N, q0 + kDqRows) : (W > 0 ? min(N, q0 + kDqRows + W - 1) : N);
+  const int kend = CAUSAL ? min(N, q0 + ROWS) : (W > 0 ? min(N, q0 + ROWS + W - 1) : N);
   const int ntiles = (kend + kDqKeys - 1) / kDqKeys;
   // first tile with a key inside the window of the block's first row
   const int jfirst = W > 0 ? max(0, q0 - W + 1) / kDqKeys : 0;
@@ -952,8 +954,21 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
   (void)lse;
   const int rows = VARLEN ? max_seqlen : N;
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
-  const int nqb = (rows + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
+  // 128-row blocks (4 waves) when 256-row blocks would give the CUs fewer than two workgroups
+  // each (plain dense layout only); a row's arithmetic is the same either way
+  if constexpr (!VARLEN && !EXT) {
+    if ((long long)BH * ((rows + kDqRows - 1) / kDqRows) < 2 * kNumCUs) {
+      constexpr int R = kDqRows / 2;
+      const int nqb = (rows + R - 1) / R;
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT, R>), dim3(nqb * BH), dim3(R / 32 * 64), 0,
+                         stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                         w.dsum, w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale,
+                         cu, window, slopes);
+      return hipGetLastError();
+    }
+  }
+  const int nqb = (rows + kDqRows - 1) / kDqRows;
   hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                      w.dsum, w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu,

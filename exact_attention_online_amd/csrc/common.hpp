@@ -39,6 +39,10 @@ using Par0 = std::integral_constant<int, 0>;
 using Par1 = std::integral_constant<int, 1>;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// compute units of an MI355X (gfx950); grids smaller than two workgroups per unit switch to
+// smaller row blocks
+constexpr int kNumCUs = 256;
+
 // C += A * B on one 32x32x16 MFMA; BF16 selects bfloat16, otherwise fp16 operands.
 template <bool BF16>
 __device__ __forceinline__ f32x16_t mfma32x32x16(i16x8_t a, i16x8_t b, f32x16_t c) {

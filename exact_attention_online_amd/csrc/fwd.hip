@@ -437,9 +437,6 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   }
 }
 
-// compute units of an MI355X (gfx950)
-constexpr int kNumCUs = 256;
-
 template <bool BF16, int D, int QB, int BC, bool CAUSAL, int NWV>
 static hipError_t launch_fwd_nwv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                  int Hkv, int N, float scale, hipStream_t stream) {

@@ -154,3 +154,29 @@ def test_backward_running_maximum_growth(kind, dtype, causal):
     refs = A.backward(q, k, v, do, causal, 1.0 / np.sqrt(128))
     for got, ref in zip((dq, dk, dv), refs):
         assert _err(got, ref) <= TOL[dtype] * max(1.0, np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- dQ block size chosen by grid size
+# The dQ kernel takes 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512, else 128-row blocks
+# (4 waves).  Below: 4*64*ceil(300/256) = 512 blocks, so the 8-wave path, over every output with a
+# ragged tail (300 = 256 + 44); one head alone takes the 4-wave path, and a row's arithmetic is the
+# same in both, so its dQ agrees bit for bit.  One query head per K/V head: grouped sums are covered
+# above; summed over 4 heads, dK reaches |4..8| where a bf16 step is 0.0156, and over the 2.4M
+# outputs of this shape the largest grouped dK error came to 0.034, past the absolute bar.
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_large_grid_full_and_block_size_invariance(dtype, d, causal):
+    B, Hq, Hkv, N = 4, 64, 64, 300
+    assert B * Hq * ((N + 255) // 256) >= 512
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, dtype, seed=90 + d + causal)
+    dq, dk, dv = _gpu_grads(q, k, v, do, causal)
+    rq, rk, rv = A.backward(q, k, v, do, causal, 1.0 / np.sqrt(d))
+    assert _err(dq, rq) <= TOL[dtype]
+    assert _err(dk, rk) <= TOL[dtype]
+    assert _err(dv, rv) <= TOL[dtype]
+    G = Hq // Hkv
+    for b, h in ((0, 0), (2, 37), (3, 63)):
+        g = h // G
+        dq1, _, _ = _gpu_grads(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                               do[b:b + 1, h:h + 1], causal)
+        assert torch.equal(dq1[0, 0].cpu(), dq[b, h].cpu()), (b, h)
