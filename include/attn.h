@@ -65,6 +65,9 @@ typedef enum {
  *   ATTN_FP8_E4M3 only: q_descale, k_descale, v_descale are float [B,H,ceil(N/128)] (H = Hq for
  *   q, Hkv for k and v): the value of a stored code x in rows 128*i .. 128*i+127 of a head is
  *   e4m3(x) * descale[i].  They must be NULL for ATTN_F16 / ATTN_BF16.
+ *   ATTN_F16 / ATTN_BF16 results are deterministic, and a head's o and lse are bit-identical
+ *   whatever the other heads and batch entries of the call are (the query-block size picked
+ *   from the grid size does not change a row's arithmetic).
  * Returns an attn_status_t. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
@@ -149,6 +152,8 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
  *   `dtype`; dk and dv are summed over the query heads that share each K/V head.
  *   workspace: device memory of at least attn_bwd_workspace_size() bytes, 256-byte aligned,
  *   owned by the caller; its contents on entry do not matter and are clobbered.
+ *   No atomics: results are deterministic, and a head's dq is bit-identical whatever the other
+ *   heads and batch entries of the call are.
  * Returns an attn_status_t. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv,
