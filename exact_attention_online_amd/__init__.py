@@ -12,10 +12,10 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "attention", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3",
+    "fwd_splitkv", "splitkv_workspace_size", "attention", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
 ]
 
-F16, BF16, FP8_E4M3 = 0, 1, 2
+F16, BF16, FP8_E4M3, F32 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
            "attn_status_string")
@@ -46,23 +46,23 @@ def load():
     lib.attn_fwd.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i] * 5
     lib.attn_bwd_workspace_size.restype = sz
-    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.attn_bwd.restype = i
     lib.attn_bwd_preprocess.argtypes = [vp] * 5 + [i] * 6 + [vp, sz, vp]
     lib.attn_bwd_preprocess.restype = i
-    lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.attn_bwd_dkdv.restype = i
-    lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_bwd_dq.argtypes = [vp] * 6 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
     lib.attn_fwd_ext.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, vp]
     lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 7 + [f, i, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_ext.restype = i
-    lib.attn_bwd_ext.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, vp, sz, vp]
+    lib.attn_bwd_ext.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, i, vp, vp, sz, vp]
     lib.attn_bwd_ext.restype = i
     lib.attn_bwd_varlen_workspace_size.argtypes = [i] * 5
     lib.attn_bwd_varlen_workspace_size.restype = sz
-    lib.attn_bwd_varlen.argtypes = [vp] * 10 + [i] * 7 + [f, i, vp, sz, vp]
+    lib.attn_bwd_varlen.argtypes = [vp] * 10 + [i] * 7 + [f, i, i, vp, sz, vp]
     lib.attn_bwd_varlen.restype = i
     lib.attn_fwd_splitkv_workspace_size.argtypes = [i] * 7
     lib.attn_fwd_splitkv_workspace_size.restype = sz
@@ -94,6 +94,16 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
     raise AttnError(f"unsupported dtype {t.dtype} (expected float16 or bfloat16)")
+
+
+def _grad_dtype(q, grad_dtype):
+    """(torch dtype, ABI code) of the gradients: the input dtype (None) or float32."""
+    torch = _torch()
+    if grad_dtype is None or grad_dtype == q.dtype:
+        return q.dtype, _dtype_code(q)
+    if grad_dtype == torch.float32:
+        return torch.float32, F32
+    raise AttnError(f"grad_dtype must be None, {q.dtype} or torch.float32, got {grad_dtype}")
 
 
 def _stream(device):
@@ -245,11 +255,13 @@ def bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None,
-        dq=None, dk=None, dv=None):
-    """dQ, dK, dV of L = <O, dO>; recomputes the probabilities from q, k, v and lse."""
+        dq=None, dk=None, dv=None, grad_dtype=None):
+    """dQ, dK, dV of L = <O, dO>; recomputes the probabilities from q, k, v and lse.  The gradients
+    come in q's dtype, or in float32 with grad_dtype=torch.float32."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     dt = _dtype_code(q)
+    gdt, gcode = _grad_dtype(q, grad_dtype)
     for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise AttnError("o and do must match q in shape, dtype and layout")
@@ -259,24 +271,25 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     need = bwd_workspace_size(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q, dtype=gdt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=gdt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=gdt) if dv is None else dv
     _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
-         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
-         dv=(dv, v.shape, v.dtype))
+         workspace=(workspace, None, None), dq=(dq, q.shape, gdt), dk=(dk, k.shape, gdt),
+         dv=(dv, v.shape, gdt))
     _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                           B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, _ptr(workspace),
+                           B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, gcode, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
 
 def bwd_ext(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, window: int = 0, alibi_slopes=None,
-            workspace=None, dq=None, dk=None, dv=None):
-    """Gradients of attn_fwd_ext (same window and ALiBi slopes); o, lse from fwd_ext."""
+            workspace=None, dq=None, dk=None, dv=None, grad_dtype=None):
+    """Gradients of attn_fwd_ext (same window and ALiBi slopes); o, lse from fwd_ext; grad_dtype as for bwd."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     dt = _dtype_code(q)
+    gdt, gcode = _grad_dtype(q, grad_dtype)
     for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise AttnError("o and do must match q in shape, dtype and layout")
@@ -292,14 +305,14 @@ def bwd_ext(q, k, v, o, do, lse, causal: bool = False, scale: float | None = Non
     need = bwd_workspace_size(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q, dtype=gdt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=gdt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=gdt) if dv is None else dv
     _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
-         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
-         dv=(dv, v.shape, v.dtype))
+         workspace=(workspace, None, None), dq=(dq, q.shape, gdt), dk=(dk, k.shape, gdt),
+         dv=(dv, v.shape, gdt))
     _check(load().attn_bwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                               _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, int(window), sl,
+                               _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), scale, dt, gcode, int(window), sl,
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
@@ -309,10 +322,10 @@ def bwd_varlen_workspace_size(B, Hq, Hkv, max_seqlen, d) -> int:
 
 
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
-               workspace=None, dq=None, dk=None, dv=None):
+               workspace=None, dq=None, dk=None, dv=None, grad_dtype=None):
     """dQ [Hq,T,d], dK, dV [Hkv,T,d] for sequences packed along T, with o, lse from fwd_varlen (same
     cu_seqlens, max_seqlen, causal flag and scale).  Rows outside every sequence come back as zeros
-    when the outputs are allocated here."""
+    when the outputs are allocated here; grad_dtype as for bwd."""
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
         raise AttnError(f"expected q [Hq,T,d], k/v [Hkv,T,d]; got {tuple(q.shape)}, {tuple(k.shape)}")
@@ -332,32 +345,35 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, causal: bool = 
         raise AttnError("cu_seqlens must be an int32 device tensor [B+1]")
     B = cu_seqlens.numel() - 1
     dt = _dtype_code(q)
+    gdt, gcode = _grad_dtype(q, grad_dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = bwd_varlen_workspace_size(B, Hq, Hkv, int(max_seqlen), d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.zeros_like(q) if dq is None else dq
-    dk = torch.zeros_like(k) if dk is None else dk
-    dv = torch.zeros_like(v) if dv is None else dv
+    dq = torch.zeros_like(q, dtype=gdt) if dq is None else dq
+    dk = torch.zeros_like(k, dtype=gdt) if dk is None else dk
+    dv = torch.zeros_like(v, dtype=gdt) if dv is None else dv
     _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (Hq, T), torch.float32),
          cu_seqlens=(cu_seqlens, (B + 1,), torch.int32), workspace=(workspace, None, None),
-         dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype), dv=(dv, v.shape, v.dtype))
+         dq=(dq, q.shape, gdt), dk=(dk, k.shape, gdt), dv=(dv, v.shape, gdt))
     _check(load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                   _ptr(dv), _ptr(cu_seqlens.contiguous()), B, Hq, Hkv, T, int(max_seqlen), d,
-                                  int(bool(causal)), scale, dt, _ptr(workspace),
+                                  int(bool(causal)), scale, dt, gcode, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
 
 def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, between=None):
     """attn_bwd as its three phases (preprocess, dK/dV, dQ); ``between(i)`` (if given) is called
-    before phase i = 0, 1, 2 and after the last one with i = 3, e.g. to record stream events."""
+    before phase i = 0, 1, 2 and after the last one with i = 3, e.g. to record stream events.
+    The gradients come in dq's dtype (q's dtype or float32)."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     dt = _dtype_code(q)
+    gdt, gcode = _grad_dtype(q, dq.dtype)
     _req(q.device, o=(o, q.shape, q.dtype), do=(do, q.shape, q.dtype), lse=(lse, (B, Hq, N), torch.float32),
-         workspace=(workspace, None, None), dq=(dq, q.shape, q.dtype), dk=(dk, k.shape, k.dtype),
-         dv=(dv, v.shape, v.dtype))
+         workspace=(workspace, None, None), dq=(dq, q.shape, gdt), dk=(dk, k.shape, gdt),
+         dv=(dv, v.shape, gdt))
     lib, st = load(), _stream(q.device)
     wsb = workspace.numel() * workspace.element_size()
     hook = between or (lambda i: None)
@@ -367,10 +383,10 @@ def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, betwee
                                    _ptr(workspace), wsb, st))
     hook(1)
     _check(lib.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
-                             causal, scale, dt, _ptr(workspace), wsb, st))
+                             causal, scale, dt, gcode, _ptr(workspace), wsb, st))
     hook(2)
     _check(lib.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq), B, Hq, Hkv, N, d, causal,
-                           scale, dt, _ptr(workspace), wsb, st))
+                           scale, dt, gcode, _ptr(workspace), wsb, st))
     hook(3)
     return dq, dk, dv
 

@@ -17,16 +17,18 @@ hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const voi
                           int max_seqlen = 0, const int* cu = nullptr);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                           const void* workspace, hipStream_t stream, int max_seqlen = 0, const int* cu = nullptr);
+                           bool out32, const void* workspace, hipStream_t stream, int max_seqlen = 0,
+                           const int* cu = nullptr);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
-                         int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                         int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16, bool out32,
                          const void* workspace, hipStream_t stream, int max_seqlen = 0, const int* cu = nullptr);
 hipError_t launch_bwd_dkdv_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale,
-                               bool bf16, const void* workspace, hipStream_t stream, int window, const float* slopes);
+                               bool bf16, bool out32, const void* workspace, hipStream_t stream, int window,
+                               const float* slopes);
 hipError_t launch_bwd_dq_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                              void* dq, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                             const void* workspace, hipStream_t stream, int window, const float* slopes);
+                             bool out32, const void* workspace, hipStream_t stream, int window, const float* slopes);
 hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                           int N, int d, bool causal, float scale, bool bf16, int window, const float* slopes,
                           hipStream_t stream);
@@ -140,11 +142,12 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
 
 // Shared checks of the backward entry points (pointer list, sizes, scale, dtype, workspace).
 static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int Hkv, int N, int d, float scale,
-                     int dtype, const void* workspace, size_t workspace_bytes) {
+                     int dtype, int grad_dtype, const void* workspace, size_t workspace_bytes) {
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_INVALID;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  if (grad_dtype != dtype && grad_dtype != ATTN_F32) return ATTN_ERR_INVALID;
   const int st = check_sizes(B, Hq, Hkv, N, d);
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
@@ -155,7 +158,7 @@ static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int
 int attn_bwd_preprocess(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
                         int Hq, int Hkv, int N, int d, int dtype, void* workspace, size_t workspace_bytes,
                         attn_stream_t stream) {
-  const int st = check_bwd({q, k, o, dout, lse}, B, Hq, Hkv, N, d, 1.f, dtype, workspace, workspace_bytes);
+  const int st = check_bwd({q, k, o, dout, lse}, B, Hq, Hkv, N, d, 1.f, dtype, dtype, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   return eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, dtype == ATTN_BF16, workspace,
                              (hipStream_t)stream) == hipSuccess
@@ -163,62 +166,62 @@ int attn_bwd_preprocess(const void* q, const void* k, const void* o, const void*
 }
 
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
-                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, int grad_dtype,
                   const void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({q, k, v, dout, lse, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
-                           workspace_bytes);
+  const int st = check_bwd({q, k, v, dout, lse, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, grad_dtype,
+                           workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   return eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
-                              dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
+                              dtype == ATTN_BF16, grad_dtype == ATTN_F32, workspace, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq, int B,
-                int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, const void* workspace,
-                size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({q, k, v, dout, lse, dq}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
+                int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, int grad_dtype,
+                const void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, dout, lse, dq}, B, Hq, Hkv, N, d, softmax_scale, dtype, grad_dtype, workspace,
                            workspace_bytes);
   if (st != ATTN_OK) return st;
   return eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale,
-                            dtype == ATTN_BF16, workspace, (hipStream_t)stream) == hipSuccess
+                            dtype == ATTN_BF16, grad_dtype == ATTN_F32, workspace, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
              void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
-             void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
-                           workspace_bytes);
+             int grad_dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, grad_dtype,
+                           workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  const bool bf16 = dtype == ATTN_BF16;
+  const bool bf16 = dtype == ATTN_BF16, out32 = grad_dtype == ATTN_F32;
   const hipStream_t s = (hipStream_t)stream;
   if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace,
-                           s) != hipSuccess)
+  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, out32,
+                           workspace, s) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s) !=
-      hipSuccess)
+  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, out32,
+                         workspace, s) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
 int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
-                 int dtype, int window, const float* alibi_slopes, void* workspace, size_t workspace_bytes,
-                 attn_stream_t stream) {
-  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, workspace,
-                           workspace_bytes);
+                 int dtype, int grad_dtype, int window, const float* alibi_slopes, void* workspace,
+                 size_t workspace_bytes, attn_stream_t stream) {
+  const int st = check_bwd({q, k, v, o, dout, lse, dq, dk, dv}, B, Hq, Hkv, N, d, softmax_scale, dtype, grad_dtype,
+                           workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   if (window < 0) return ATTN_ERR_INVALID;
   if (alibi_slopes != nullptr && ((uintptr_t)alibi_slopes & 3u) != 0) return ATTN_ERR_INVALID;
-  const bool bf16 = dtype == ATTN_BF16;
+  const bool bf16 = dtype == ATTN_BF16, out32 = grad_dtype == ATTN_F32;
   const hipStream_t s = (hipStream_t)stream;
   if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, N, d, bf16, workspace, s) != hipSuccess) return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dkdv_ext(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16,
+  if (eao::launch_bwd_dkdv_ext(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, out32,
                                workspace, s, window, alibi_slopes) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dq_ext(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, workspace, s,
-                             window, alibi_slopes) != hipSuccess)
+  if (eao::launch_bwd_dq_ext(q, k, v, dout, lse, dq, B, Hq, Hkv, N, d, causal != 0, softmax_scale, bf16, out32,
+                             workspace, s, window, alibi_slopes) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -230,13 +233,14 @@ size_t attn_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int max_seqlen, in
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int Hq, int Hkv, int T,
-                    int max_seqlen, int d, int causal, float softmax_scale, int dtype, void* workspace,
-                    size_t workspace_bytes, attn_stream_t stream) {
+                    int max_seqlen, int d, int causal, float softmax_scale, int dtype, int grad_dtype,
+                    void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   for (const void* p : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(p)) return ATTN_ERR_INVALID;
   if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u) != 0) return ATTN_ERR_INVALID;
   if (!scale_ok(softmax_scale) || max_seqlen < 1 || max_seqlen > T) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  if (grad_dtype != dtype && grad_dtype != ATTN_F32) return ATTN_ERR_INVALID;
   // the packed tensors are one batch of T rows per head; the workspace is B sequences of max_seqlen
   int st = check_sizes(1, Hq, Hkv, T, d);
   if (st != ATTN_OK) return st;
@@ -244,16 +248,16 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
   if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d)) return ATTN_ERR_WORKSPACE;
-  const bool bf16 = dtype == ATTN_BF16;
+  const bool bf16 = dtype == ATTN_BF16, out32 = grad_dtype == ATTN_F32;
   const hipStream_t s = (hipStream_t)stream;
   if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, T, d, bf16, workspace, s, max_seqlen, cu_seqlens) !=
       hipSuccess)
     return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, workspace,
-                           s, max_seqlen, cu_seqlens) != hipSuccess)
+  if (eao::launch_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, out32,
+                           workspace, s, max_seqlen, cu_seqlens) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, workspace, s,
-                         max_seqlen, cu_seqlens) != hipSuccess)
+  if (eao::launch_bwd_dq(q, k, v, dout, lse, dq, B, Hq, Hkv, T, d, causal != 0, softmax_scale, bf16, out32,
+                         workspace, s, max_seqlen, cu_seqlens) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

@@ -216,6 +216,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   write_transposed<D, STR>(tdo, dOT + dst, tid);
 }
 
+// One gradient row from an accumulator whose register r of block db holds column
+// 32db + 8(r/4) + 4g + r%4, times f: stored as float (out32) or rounded to the input type.
+// `elem` is the row's first element; the row is D = 32 * DB values.
+template <bool BF16, int DB>
+__device__ __forceinline__ void store_row(void* __restrict__ base, size_t elem, const f32x16_t (&acc)[DB], float f,
+                                          int g, int out32) {
+  if (out32) {
+    float* dst = (float*)base + elem;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        *(float4*)(dst + d0) = float4{acc[db][4 * rr + 0] * f, acc[db][4 * rr + 1] * f, acc[db][4 * rr + 2] * f,
+                                      acc[db][4 * rr + 3] * f};
+      }
+  } else {
+    uint16_t* dst = (uint16_t*)base + elem;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        uint2 pk;
+        pk.x = pack2<BF16>(acc[db][4 * rr + 0] * f, acc[db][4 * rr + 1] * f);
+        pk.y = pack2<BF16>(acc[db][4 * rr + 2] * f, acc[db][4 * rr + 3] * f);
+        *(uint2*)(dst + d0) = pk;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ 2. dK, dV
 // One workgroup of 8 waves per (batch, K/V head, block of 128 keys).  The waves come in two
 // roles over the same four quarters of 32 keys, one wave of each role per SIMD:
@@ -241,9 +272,9 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
-    const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
-    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes) {
+    const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, void* __restrict__ dK,
+    void* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
+    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes, int out32) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = 8;                              // waves per workgroup
   constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
@@ -592,18 +623,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
   const int key = kw + l32;
   if (key < N) {
-    uint16_t* dst = (role == 0 ? dV : dK) + kv_off + (size_t)key * D;
-    const float f = role == 0 ? 1.f : scale;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * db + 8 * rr + 4 * g;
-        uint2 pk;
-        pk.x = pack2<BF16>(acc[db][4 * rr + 0] * f, acc[db][4 * rr + 1] * f);
-        pk.y = pack2<BF16>(acc[db][4 * rr + 2] * f, acc[db][4 * rr + 3] * f);
-        *(uint2*)(dst + d0) = pk;
-      }
+    store_row<BF16, DB>(role == 0 ? dV : dK, kv_off + (size_t)key * D, acc, role == 0 ? 1.f : scale, g, out32);
   }
 }
 
@@ -622,9 +642,9 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, 
 __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
-    const uint16_t* __restrict__ KT, uint16_t* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
+    const uint16_t* __restrict__ KT, void* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
     float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens, int window,
-    const float* __restrict__ slopes) {
+    const float* __restrict__ slopes, int out32) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = ROWS / 32;                     // waves per workgroup
   constexpr int TILE = kDqKeys * D;                 // 16-bit elements per tile
@@ -898,19 +918,7 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   for (; j < ntiles; ++j) idle(j);
 
   // epilogue: dQ = scale * dQ^T; register r of block db holds d = 32db + 8(r/4) + 4g + r%4
-  if (qrow < N) {
-    uint16_t* dqp = dQ + (q_row0 + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * db + 8 * rr + 4 * g;
-        uint2 pk;
-        pk.x = pack2<BF16>(acc[db][4 * rr + 0] * scale, acc[db][4 * rr + 1] * scale);
-        pk.y = pack2<BF16>(acc[db][4 * rr + 2] * scale, acc[db][4 * rr + 3] * scale);
-        *(uint2*)(dqp + d0) = pk;
-      }
-  }
+  if (qrow < N) store_row<BF16, DB>(dQ, (q_row0 + qrow) * D, acc, scale, g, out32);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -933,7 +941,7 @@ static hipError_t launch_pre_t(const void* q, const void* k, const void* o, cons
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
 static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu,
-                                float scale, const void* workspace, hipStream_t stream, int window = 0,
+                                float scale, bool out32, const void* workspace, hipStream_t stream, int window = 0,
                                 const float* slopes = nullptr) {
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
   const int rows = VARLEN ? max_seqlen : N;
@@ -941,15 +949,15 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
   const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
-                     w.lse2, w.qt, w.dot, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e,
-                     scale, cu, window, slopes);
+                     w.lse2, w.qt, w.dot, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
+                     slopes, (int)out32);
   return hipGetLastError();
 }
 
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
 static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               void* dq, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu, float scale,
-                              const void* workspace, hipStream_t stream, int window = 0,
+                              bool out32, const void* workspace, hipStream_t stream, int window = 0,
                               const float* slopes = nullptr) {
   (void)lse;
   const int rows = VARLEN ? max_seqlen : N;
@@ -963,16 +971,16 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
       const int nqb = (rows + R - 1) / R;
       hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT, R>), dim3(nqb * BH), dim3(R / 32 * 64), 0,
                          stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                         w.dsum, w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale,
-                         cu, window, slopes);
+                         w.dsum, w.lse2, w.kt, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
+                         slopes, (int)out32);
       return hipGetLastError();
     }
   }
   const int nqb = (rows + kDqRows - 1) / kDqRows;
   hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                     w.dsum, w.lse2, w.kt, (uint16_t*)dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu,
-                     window, slopes);
+                     w.dsum, w.lse2, w.kt, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
+                     slopes, (int)out32);
   return hipGetLastError();
 }
 
@@ -1009,51 +1017,53 @@ hipError_t launch_bwd_pre(const void* q, const void* k, const void* o, const voi
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                           const void* workspace, hipStream_t stream, int max_seqlen, const int* cu) {
+                           bool out32, const void* workspace, hipStream_t stream, int max_seqlen, const int* cu) {
   if (cu != nullptr) {
-    EAO_DISPATCH_V(launch_dkdv_t, true, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, max_seqlen, cu, scale, workspace,
-                   stream)
+    EAO_DISPATCH_V(launch_dkdv_t, true, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, max_seqlen, cu, scale, out32,
+                   workspace, stream)
   }
-  EAO_DISPATCH_V(launch_dkdv_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, cu, scale, workspace, stream)
+  EAO_DISPATCH_V(launch_dkdv_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, cu, scale, out32, workspace,
+                 stream)
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
-                         int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
+                         int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16, bool out32,
                          const void* workspace, hipStream_t stream, int max_seqlen, const int* cu) {
   if (cu != nullptr) {
-    EAO_DISPATCH_V(launch_dq_t, true, q, k, v, dout, lse, dq, B, Hq, Hkv, N, max_seqlen, cu, scale, workspace, stream)
+    EAO_DISPATCH_V(launch_dq_t, true, q, k, v, dout, lse, dq, B, Hq, Hkv, N, max_seqlen, cu, scale, out32, workspace,
+                   stream)
   }
-  EAO_DISPATCH_V(launch_dq_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, cu, scale, workspace, stream)
+  EAO_DISPATCH_V(launch_dq_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, cu, scale, out32, workspace, stream)
 }
 // sliding window and/or ALiBi (dense layout): the dK/dV and dQ phases with EXT
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
 static hipError_t launch_dkdv_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                    void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                                    void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, bool out32,
                                     const void* workspace, hipStream_t stream, int window, const float* slopes) {
   return launch_dkdv_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, nullptr, scale,
-                                                      workspace, stream, window, slopes);
+                                                      out32, workspace, stream, window, slopes);
 }
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
 static hipError_t launch_dq_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                  void* dq, int B, int Hq, int Hkv, int N, float scale, const void* workspace,
-                                  hipStream_t stream, int window, const float* slopes) {
+                                  void* dq, int B, int Hq, int Hkv, int N, float scale, bool out32,
+                                  const void* workspace, hipStream_t stream, int window, const float* slopes) {
   return launch_dq_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, nullptr, scale,
-                                                    workspace, stream, window, slopes);
+                                                    out32, workspace, stream, window, slopes);
 }
 
 hipError_t launch_bwd_dkdv_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, bool causal, float scale,
-                               bool bf16, const void* workspace, hipStream_t stream, int window,
+                               bool bf16, bool out32, const void* workspace, hipStream_t stream, int window,
                                const float* slopes) {
-  EAO_DISPATCH_V(launch_dkdv_ext_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, scale, workspace, stream,
-                 window, slopes)
+  EAO_DISPATCH_V(launch_dkdv_ext_t, false, q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, scale, out32, workspace,
+                 stream, window, slopes)
 }
 
 hipError_t launch_bwd_dq_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                              void* dq, int B, int Hq, int Hkv, int N, int d, bool causal, float scale, bool bf16,
-                             const void* workspace, hipStream_t stream, int window, const float* slopes) {
-  EAO_DISPATCH_V(launch_dq_ext_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, scale, workspace, stream, window,
-                 slopes)
+                             bool out32, const void* workspace, hipStream_t stream, int window, const float* slopes) {
+  EAO_DISPATCH_V(launch_dq_ext_t, false, q, k, v, dout, lse, dq, B, Hq, Hkv, N, scale, out32, workspace, stream,
+                 window, slopes)
 }
 #undef EAO_DISPATCH_V
 

@@ -46,9 +46,10 @@ extern "C" {
 typedef void* attn_stream_t; /* a hipStream_t */
 
 typedef enum {
-  ATTN_F16 = 0,      /* IEEE binary16 storage */
-  ATTN_BF16 = 1,     /* bfloat16 storage */
-  ATTN_FP8_E4M3 = 2  /* OCP FP8 E4M3 (e4m3fn) storage with per-block float scales */
+  ATTN_F16 = 0,       /* IEEE binary16 storage */
+  ATTN_BF16 = 1,      /* bfloat16 storage */
+  ATTN_FP8_E4M3 = 2,  /* OCP FP8 E4M3 (e4m3fn) storage with per-block float scales */
+  ATTN_F32 = 3        /* IEEE binary32: only as the gradient dtype of a backward call */
 } attn_dtype_t;
 
 typedef enum {
@@ -108,13 +109,14 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * Partitioning", OpenReview discussion, author responses: ALiBi and local attention;
  * "FlashAttention (NeurIPS 2022)" notes, "Backward - Recomputation").  The bias does not depend
  * on q or k, so the gradients keep the form of attn_bwd with P recomputed under the same mask
- * and bias.  Arguments as for attn_bwd (same workspace size, attn_bwd_workspace_size), with
- * o and lse from attn_fwd_ext and the same causal flag, scale, window and alibi_slopes.
+ * and bias.  Arguments as for attn_bwd (same workspace size, attn_bwd_workspace_size, and the
+ * same grad_dtype choice), with o and lse from attn_fwd_ext and the same causal flag, scale,
+ * window and alibi_slopes.
  * window 0 and NULL slopes give exactly attn_bwd's gradients up to rounding order.
  * Returns an attn_status_t. */
 int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                 int d, int causal, float softmax_scale, int dtype, int window,
+                 int d, int causal, float softmax_scale, int dtype, int grad_dtype, int window,
                  const float* alibi_slopes, void* workspace, size_t workspace_bytes,
                  attn_stream_t stream);
 
@@ -125,9 +127,9 @@ int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, con
  * gradients are those attn_bwd gives for that sequence alone.
  *   q, o, dout [Hq,T,d], k, v [Hkv,T,d] in `dtype` (ATTN_F16 / ATTN_BF16), lse [Hq,T] float from
  *   attn_fwd_varlen with the same cu_seqlens, causal flag and scale; cu_seqlens, B, T and
- *   max_seqlen as for attn_fwd_varlen.  Outputs dq [Hq,T,d], dk, dv [Hkv,T,d] in `dtype`, dk and
- *   dv summed over the query heads that share each K/V head; rows that belong to no sequence
- *   (past cu_seqlens[B]) are not written.
+ *   max_seqlen as for attn_fwd_varlen.  Outputs dq [Hq,T,d], dk, dv [Hkv,T,d] in `grad_dtype`
+ *   (`dtype` or ATTN_F32, as for attn_bwd), dk and dv summed over the query heads that share each
+ *   K/V head; rows that belong to no sequence (past cu_seqlens[B]) are not written.
  *   workspace: device memory of at least attn_bwd_varlen_workspace_size() bytes, 256-byte
  *   aligned, owned by the caller; clobbered.  A sequence longer than max_seqlen (rounded up to
  *   64) gets unspecified gradients but no access outside the buffers.
@@ -136,7 +138,8 @@ size_t attn_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int max_seqlen, in
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int B,
                     int Hq, int Hkv, int T, int max_seqlen, int d, int causal, float softmax_scale,
-                    int dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream);
+                    int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                    attn_stream_t stream);
 
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
  * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
@@ -149,7 +152,12 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
  * Recomputation"; dV = P^T dO from the FlashAttention-2 discussion).
  *   q, k, v, o, dout, lse as produced by/for attn_fwd with the same sizes, causal flag and
  *   scale; dtype ATTN_F16 or ATTN_BF16.  Outputs dq [B,Hq,N,d] and dk, dv [B,Hkv,N,d] in
- *   `dtype`; dk and dv are summed over the query heads that share each K/V head.
+ *   `grad_dtype`; dk and dv are summed over the query heads that share each K/V head.
+ *   grad_dtype: `dtype` (the fp32 accumulators rounded to nearest even) or ATTN_F32 (the
+ *   accumulators themselves, 4 bytes per element).  Anything else is ATTN_ERR_INVALID.  A group
+ *   sum of several query heads can exceed 8 in magnitude, where half a bfloat16 step (2^-5) is
+ *   already more than an absolute error bound of 3e-2; ATTN_F32 keeps such sums free of that
+ *   rounding.
  *   workspace: device memory of at least attn_bwd_workspace_size() bytes, 256-byte aligned,
  *   owned by the caller; its contents on entry do not matter and are clobbered.
  *   No atomics: results are deterministic, and a head's dq is bit-identical whatever the other
@@ -158,7 +166,7 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv,
              int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
-             void* workspace, size_t workspace_bytes, attn_stream_t stream);
+             int grad_dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* The three phases attn_bwd runs, for callers that schedule or time them separately.  With the
  * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
@@ -168,17 +176,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  *                        dout and k into the workspace.
  *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
  *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
- * Arguments mean what they mean for attn_bwd; each returns an attn_status_t. */
+ * Arguments mean what they mean for attn_bwd (preprocess takes no grad_dtype: it writes only
+ * the workspace); each returns an attn_status_t. */
 int attn_bwd_preprocess(const void* q, const void* k, const void* o, const void* dout,
                         const float* lse, int B, int Hq, int Hkv, int N, int d, int dtype,
                         void* workspace, size_t workspace_bytes, attn_stream_t stream);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
-                  float softmax_scale, int dtype, const void* workspace, size_t workspace_bytes,
-                  attn_stream_t stream);
+                  float softmax_scale, int dtype, int grad_dtype, const void* workspace,
+                  size_t workspace_bytes, attn_stream_t stream);
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                 void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
-                int dtype, const void* workspace, size_t workspace_bytes, attn_stream_t stream);
+                int dtype, int grad_dtype, const void* workspace, size_t workspace_bytes,
+                attn_stream_t stream);
 
 /* Split-KV forward for decoding ("FlashAttention-2: Faster Attention with Better Parallelism and
  * Work Partitioning", OpenReview discussion: the author response on decoding and the review

@@ -31,3 +31,23 @@ def sample_rows(N, n_random=48, seed=0, tile=128):
         rows = set(sorted(rows)[:32]) | set(sorted(rows)[-32:])
     rows.update(rng.integers(0, N, size=n_random).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < N), dtype=np.int64)
+
+
+def half_step(ref, dtype):
+    """Half the spacing of `dtype` (fp16/bf16) numbers at |ref|: the error that storing an exact
+    value in that format can add by itself (round to nearest).  Zero for float32 outputs."""
+    if dtype == "fp32":
+        return np.zeros_like(np.asarray(ref, dtype=np.float64))
+    mant = {"bf16": 7, "fp16": 10}[dtype]
+    emin = {"bf16": -126, "fp16": -14}[dtype]
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    return np.ldexp(1.0, (e - mant - 1).astype(np.int64))
+
+
+def excess(got, ref, tol, dtype):
+    """max(|got - ref| - tol - half_step(ref)): <= 0 when every element is within the bar plus
+    the rounding of the output format."""
+    got = np.asarray(got, dtype=np.float64)
+    return float((np.abs(got - ref) - tol - half_step(ref, dtype)).max())

@@ -56,17 +56,21 @@ def test_fwd_rejects_bad_arguments(kw, code):
 
 
 def bwd(**kw):
-    a = dict(B=1, Hq=2, Hkv=1, N=64, d=128, causal=1, scale=0.1, dtype=1, ws=P, wsb=1 << 40)
+    a = dict(B=1, Hq=2, Hkv=1, N=64, d=128, causal=1, scale=0.1, dtype=1, gdt=None, ws=P, wsb=1 << 40)
     a.update(kw)
+    gdt = a["dtype"] if a["gdt"] is None else a["gdt"]
     ptrs = [a.get(n, P) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
     return eao.load().attn_bwd(*ptrs, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
-                               a["ws"], a["wsb"], NULL)
+                               gdt, a["ws"], a["wsb"], NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dq=NULL), 1), (dict(lse=ctypes.c_void_p(0x7F0000001004)), 1), (dict(Hq=5, Hkv=2), 1), (dict(N=-3), 1),
     (dict(scale=0.0), 1), (dict(dtype=3), 1), (dict(dtype=2), 2), (dict(d=32), 2), (dict(ws=NULL), 3),
     (dict(ws=ctypes.c_void_p(0x7F0000001010)), 3), (dict(wsb=100), 3), (dict(N=1 << 23), 2),
+    # gradients in the input dtype or float32 only
+    (dict(gdt=0), 1), (dict(gdt=2), 1), (dict(gdt=4), 1), (dict(dtype=0, gdt=1), 1),
+    (dict(gdt=3, dq=ctypes.c_void_p(0x7F0000001008)), 1),
 ])
 def test_bwd_rejects_bad_arguments(kw, code):
     assert bwd(**kw) == code
@@ -146,10 +150,11 @@ def test_fwd_varlen_rejects_bad_arguments():
 
 def test_bwd_varlen_rejects_bad_arguments():
     lib = eao.load()
-    # q, k, v, o, dout, lse, dq, dk, dv, cu, B, Hq, Hkv, T, max_seqlen, d, causal, scale, dtype, ws, bytes, stream
+    # q, k, v, o, dout, lse, dq, dk, dv, cu, B, Hq, Hkv, T, max_seqlen, d, causal, scale, dtype, grad dtype,
+    # ws, bytes, stream
     need = lib.attn_bwd_varlen_workspace_size(3, 4, 2, 500, 128)
     assert need == lib.attn_bwd_workspace_size(3, 4, 2, 500, 128) > 0
-    a = [P] * 10 + [3, 4, 2, 1000, 500, 128, 1, 0.1, 1, P, need, NULL]
+    a = [P] * 10 + [3, 4, 2, 1000, 500, 128, 1, 0.1, 1, 1, P, need, NULL]
     bad = list(a); bad[9] = NULL                                             # no offsets
     assert lib.attn_bwd_varlen(*bad) == 1
     bad = list(a); bad[14] = 1001                                            # max_seqlen > T
@@ -158,9 +163,11 @@ def test_bwd_varlen_rejects_bad_arguments():
     assert lib.attn_bwd_varlen(*bad) == 2
     bad = list(a); bad[18] = 2                                               # fp8
     assert lib.attn_bwd_varlen(*bad) == 2
-    bad = list(a); bad[20] = need - 1                                        # workspace too small
+    bad = list(a); bad[19] = 0                                               # fp16 gradients of bf16 inputs
+    assert lib.attn_bwd_varlen(*bad) == 1
+    bad = list(a); bad[21] = need - 1                                        # workspace too small
     assert lib.attn_bwd_varlen(*bad) == 3
-    bad = list(a); bad[19] = NULL                                            # no workspace
+    bad = list(a); bad[20] = NULL                                            # no workspace
     assert lib.attn_bwd_varlen(*bad) == 3
     bad = list(a); bad[12] = 3                                               # Hq % Hkv != 0
     assert lib.attn_bwd_varlen(*bad) != 0
@@ -170,15 +177,18 @@ def test_bwd_varlen_rejects_bad_arguments():
 def test_bwd_ext_rejects_bad_arguments():
     lib = eao.load()
     need = lib.attn_bwd_workspace_size(1, 2, 2, 100, 128)
-    # q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype, window, slopes, ws, bytes, stream
-    a = [P] * 9 + [1, 2, 2, 100, 128, 1, 0.1, 1, 4, NULL, P, need, NULL]
-    bad = list(a); bad[17] = -1                                              # negative window
+    # q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype, grad dtype, window, slopes, ws,
+    # bytes, stream
+    a = [P] * 9 + [1, 2, 2, 100, 128, 1, 0.1, 1, 3, 4, NULL, P, need, NULL]
+    bad = list(a); bad[18] = -1                                              # negative window
     assert lib.attn_bwd_ext(*bad) == 1
-    bad = list(a); bad[18] = ctypes.c_void_p(0x7F0000001002)                 # misaligned slopes
+    bad = list(a); bad[19] = ctypes.c_void_p(0x7F0000001002)                 # misaligned slopes
     assert lib.attn_bwd_ext(*bad) == 1
     bad = list(a); bad[16] = 2                                               # fp8
     assert lib.attn_bwd_ext(*bad) == 2
+    bad = list(a); bad[17] = 2                                               # fp8 gradients
+    assert lib.attn_bwd_ext(*bad) == 1
     bad = list(a); bad[13] = 96                                              # head dim
     assert lib.attn_bwd_ext(*bad) == 2
-    bad = list(a); bad[20] = need - 1                                        # workspace too small
+    bad = list(a); bad[21] = need - 1                                        # workspace too small
     assert lib.attn_bwd_ext(*bad) == 3

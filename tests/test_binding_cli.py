@@ -55,3 +55,30 @@ def test_bench_fails_loudly_without_a_gpu():
     assert r.returncode != 0
     assert "no GPU visible" in r.stderr
     assert '"value"' not in r.stdout
+
+
+def test_bench_result_check_flags_a_planted_error():
+    """bench.py's result check: the oracle's own outputs pass; one planted error past a bar fails."""
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import bench
+    from attn_inputs import WORKLOADS
+
+    w = WORKLOADS["gqa_bf16"].with_(B=1, Hq=4, Hkv=2, N=8)
+    rng = np.random.default_rng(0)
+    G = w.Hq // w.Hkv
+    outs = {1: (rng.standard_normal((1, G, 8, 128)), rng.standard_normal((1, G, 8)),
+                rng.standard_normal((1, G, 8, 128)), rng.standard_normal((1, 1, 8, 128)),
+                rng.standard_normal((1, 1, 8, 128)))}
+    full = [torch.zeros(1, 4, 8, 128, dtype=torch.float64), torch.zeros(1, 4, 8, dtype=torch.float64),
+            torch.zeros(1, 4, 8, 128, dtype=torch.float64), torch.zeros(1, 2, 8, 128, dtype=torch.float64),
+            torch.zeros(1, 2, 8, 128, dtype=torch.float64)]
+    for t, r, grouped in zip(full, outs[1], (True, True, True, False, False)):
+        sl = slice(G, 2 * G) if grouped else slice(1, 2)
+        t[:, sl] = torch.from_numpy(r)
+    rep = bench.check_results(w, full, outs)
+    assert rep["pass"] and all(v == 0.0 for v in rep["max_abs"].values())
+    full[3][0, 1, 5, 7] += 0.05          # dK past its 3e-2 bar
+    rep = bench.check_results(w, full, outs)
+    assert not rep["pass"] and rep["max_abs"]["dK"] > 0.03

@@ -43,6 +43,11 @@ def test_bwd_rejects_host_or_misshapen_arguments():
         eao.bwd(q, k, v, o, do, lse, dq=torch.empty_like(q, device="cpu"))
     with pytest.raises(eao.AttnError, match="dk"):
         eao.bwd(q, k, v, o, do, lse, dk=torch.empty(1, 2, 64, 32, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(eao.AttnError, match="grad_dtype"):
+        eao.bwd(q, k, v, o, do, lse, grad_dtype=torch.float16)
+    # float32 gradients need float32 outputs
+    with pytest.raises(eao.AttnError, match="dq"):
+        eao.bwd(q, k, v, o, do, lse, grad_dtype=torch.float32, dq=torch.empty_like(q))
 
 
 def test_varlen_rejects_host_offsets_and_outputs():

@@ -3,8 +3,15 @@
 Tolerances (max-abs over every compared element): dQ, dK, dV <= 5e-3 for fp16 and <= 3e-2 for
 bf16 on unit-normal inputs.  The GPU backward consumes the GPU forward's O and LSE (the real
 pipeline); one case feeds the oracle's O and LSE instead to isolate the backward kernels.
-Small problems are compared over every output; the large workloads over whole K/V head groups
-(every dK/dV row of the group and every dQ row of its query heads).
+Every output is compared: small problems in one oracle call, the large workloads K/V head group
+by K/V head group (every dK/dV row of the group and every dQ row of its query heads).
+
+Gradient storage.  The bars are absolute.  A dK/dV sum over a group of query heads can exceed 8
+in magnitude, where half a bfloat16 step (2^-5 = 0.03125) is itself more than 3e-2, so a bf16
+result can miss the bar by its own rounding.  The contract checks therefore read the gradients in
+float32 (grad_dtype=torch.float32: the kernels' fp32 accumulators written as they are) against
+the plain bar, and the gradients stored in the input dtype against the bar plus half a step of
+that dtype at the reference value (`gpu_util.excess`).
 """
 import numpy as np
 import pytest
@@ -12,7 +19,7 @@ import torch
 
 import exact_attention_online_amd as eao
 from attn_inputs import WORKLOADS, draw, round_to
-from gpu_util import device, f64, to_dev
+from gpu_util import device, excess, f64, to_dev
 from oracle import attention as A
 
 pytestmark = pytest.mark.gpu
@@ -25,14 +32,14 @@ def _inputs(B, Hq, Hkv, N, d, dtype, seed):
     return [round_to(x, dtype) for x in (q, k, v, do)]
 
 
-def _gpu_grads(q, k, v, do, causal, scale=None, o=None, lse=None):
+def _gpu_grads(q, k, v, do, causal, scale=None, o=None, lse=None, grad_dtype=None):
     dev = device()
     tq, tk, tv, tdo = (to_dev(x, dev) for x in (q, k, v, do))
     if o is None:
         o, lse = eao.fwd(tq, tk, tv, causal=causal, scale=scale)
     else:
         o, lse = to_dev(o, dev), to_dev(lse, dev)
-    dq, dk, dv = eao.bwd(tq, tk, tv, o, tdo, lse, causal=causal, scale=scale)
+    dq, dk, dv = eao.bwd(tq, tk, tv, o, tdo, lse, causal=causal, scale=scale, grad_dtype=grad_dtype)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -86,26 +93,46 @@ def test_custom_scale_fp16():
         assert _err(g, r) <= TOL["fp16"]
 
 
-def _group_check(w, seed, groups, row_block):
+def _every_group_check(w, seed, row_block):
+    """Every output of workload `w`: float32 gradients against the bar, gradients stored in the
+    input dtype against the bar plus half a step of that dtype; the oracle walks the K/V head
+    groups one at a time."""
     q, k, v, do = _inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, seed=seed)
-    dq, dk, dv = _gpu_grads(q, k, v, do, w.causal)
-    G = w.Hq // w.Hkv
-    for b, g in groups:
-        print(f"  oracle group b={b} g={g}", flush=True)
-        rq, rk, rv, _ = A.backward_group(q, k, v, do, w.causal, w.scale, b, g, row_block=row_block)
-        assert _err(dk[b, g], rk) <= TOL[w.dtype], ("dk", b, g)
-        assert _err(dv[b, g], rv) <= TOL[w.dtype], ("dv", b, g)
-        assert _err(dq[b, g * G:(g + 1) * G], rq) <= TOL[w.dtype], ("dq", b, g)
-    for t in (dq, dk, dv):
+    dev = device()
+    tq, tk, tv, tdo = (to_dev(x, dev) for x in (q, k, v, do))
+    o, lse = eao.fwd(tq, tk, tv, causal=w.causal)
+    g32 = eao.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, grad_dtype=torch.float32)
+    g16 = eao.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal)
+    torch.cuda.synchronize()
+    for t in (*g32, *g16):
         assert torch.isfinite(t).all()
+    q64, k64, v64, do64 = (f64(x) for x in (q, k, v, do))
+    G = w.Hq // w.Hkv
+    tol = TOL[w.dtype]
+    worst = {}
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            rq, rk, rv, _ = A.backward_group(q64, k64, v64, do64, w.causal, w.scale, b, g, row_block=row_block)
+            for name, idx, ref in (("dq", (b, slice(g * G, (g + 1) * G)), rq), ("dk", (b, g), rk), ("dv", (b, g), rv)):
+                i = "dq dk dv".split().index(name)
+                e32 = _err(g32[i][idx], ref)
+                x16 = excess(f64(g16[i][idx]), ref, tol, w.dtype)
+                worst[name] = max(worst.get(name, 0.0), e32)
+                assert e32 <= tol, (name, b, g, e32)
+                assert x16 <= 0.0, (name, b, g, x16)
+        print(f"  batch {b}: worst float32 gradient errors so far {worst}", flush=True)
 
 
-def test_gqa_workload_groups():
-    _group_check(WORKLOADS["gqa_bf16"], 4, [(0, 0), (3, 7)], row_block=1024)
+@pytest.mark.timeout(900)
+def test_gqa_workload_every_group():
+    """Grouped-query workload (B=4, Hq=32, Hkv=8, N=4096, d=128, bf16, causal): all 32 K/V groups."""
+    _every_group_check(WORKLOADS["gqa_bf16"], 4, row_block=1024)
 
 
-def test_long_workload_one_head():
-    _group_check(WORKLOADS["long_bf16"], 3, [(0, 5)], row_block=1024)
+@pytest.mark.timeout(900)
+def test_long_workload_every_head():
+    """Long workload (B=1, H=16, N=16384, d=128, bf16, causal): all 16 heads."""
+    _every_group_check(WORKLOADS["long_bf16"], 3, row_block=1024)
 
 
 # ---------------------------------------------------------------- invariants on the device
@@ -159,24 +186,42 @@ def test_backward_running_maximum_growth(kind, dtype, causal):
 # ---------------------------------------------------------------- dQ block size chosen by grid size
 # The dQ kernel takes 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512, else 128-row blocks
 # (4 waves).  Below: 4*64*ceil(300/256) = 512 blocks, so the 8-wave path, over every output with a
-# ragged tail (300 = 256 + 44); one head alone takes the 4-wave path, and a row's arithmetic is the
-# same in both, so its dQ agrees bit for bit.  One query head per K/V head: grouped sums are covered
-# above; summed over 4 heads, dK reaches |4..8| where a bf16 step is 0.0156, and over the 2.4M
-# outputs of this shape the largest grouped dK error came to 0.034, past the absolute bar.
+# ragged tail (300 = 256 + 44), four query heads per K/V head; one head alone takes the 4-wave
+# path, and a row's arithmetic is the same in both, so its dQ agrees bit for bit.  Summed over four
+# query heads dV reaches |11| here, where half a bf16 step is 2^-5 > 3e-2: float32 gradients are
+# held to the bar, bf16 gradients to the bar plus their own rounding.
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_large_grid_full_and_block_size_invariance(dtype, d, causal):
-    B, Hq, Hkv, N = 4, 64, 64, 300
+    B, Hq, Hkv, N = 4, 64, 16, 300
     assert B * Hq * ((N + 255) // 256) >= 512
     q, k, v, do = _inputs(B, Hq, Hkv, N, d, dtype, seed=90 + d + causal)
-    dq, dk, dv = _gpu_grads(q, k, v, do, causal)
+    dq, dk, dv = _gpu_grads(q, k, v, do, causal, grad_dtype=torch.float32)
+    dq16, dk16, dv16 = _gpu_grads(q, k, v, do, causal)
     rq, rk, rv = A.backward(q, k, v, do, causal, 1.0 / np.sqrt(d))
-    assert _err(dq, rq) <= TOL[dtype]
-    assert _err(dk, rk) <= TOL[dtype]
-    assert _err(dv, rv) <= TOL[dtype]
+    for got, got16, ref in ((dq, dq16, rq), (dk, dk16, rk), (dv, dv16, rv)):
+        assert _err(got, ref) <= TOL[dtype]
+        assert excess(f64(got16), ref, TOL[dtype], dtype) <= 0.0
+        # the stored gradients are the float32 ones rounded to nearest
+        assert torch.equal(got.to(got16.dtype), got16)
     G = Hq // Hkv
     for b, h in ((0, 0), (2, 37), (3, 63)):
         g = h // G
         dq1, _, _ = _gpu_grads(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
                                do[b:b + 1, h:h + 1], causal)
-        assert torch.equal(dq1[0, 0].cpu(), dq[b, h].cpu()), (b, h)
+        assert torch.equal(dq1[0, 0].cpu(), dq16[b, h].cpu()), (b, h)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_float32_gradients_are_the_accumulators(dtype):
+    """Both gradient dtypes come from the same accumulators: the stored ones are the float32
+    ones rounded to nearest even, bit for bit, across the three phases as well."""
+    B, Hq, Hkv, N, d = 2, 6, 2, 333, 128
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, dtype, seed=83)
+    g32 = _gpu_grads(q, k, v, do, True, grad_dtype=torch.float32)
+    g16 = _gpu_grads(q, k, v, do, True)
+    refs = A.backward(q, k, v, do, True, 1.0 / np.sqrt(d))
+    for a, b, r in zip(g32, g16, refs):
+        assert a.dtype == torch.float32 and b.dtype == q.dtype
+        assert torch.equal(a.to(b.dtype), b)
+        assert _err(a, r) <= TOL[dtype]

@@ -93,3 +93,22 @@ def test_bwd_ext_long_workload_invariants():
     dof = do.to(torch.float64).numpy()
     np.testing.assert_allclose(dv[0].sum(axis=1), dof[0].sum(axis=1), atol=2.0)
     assert np.abs(dk[0].sum(axis=1)).max() <= 2.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ext_float32_gradients(causal):
+    """grad_dtype=float32: the accumulators unrounded, within the bar; rounded, the bf16 result."""
+    q, k, v, do = _inputs(2, 8, 2, 400, 128, "bf16", seed=15)
+    sl = _slopes(8)
+    dev = device()
+    ts = torch.from_numpy(sl).to(dev)
+    tq, tk, tv, tdo = (to_dev(x, dev) for x in (q, k, v, do))
+    o, lse = eao.fwd_ext(tq, tk, tv, causal=causal, window=150, alibi_slopes=ts)
+    g16 = eao.bwd_ext(tq, tk, tv, o, tdo, lse, causal=causal, window=150, alibi_slopes=ts)
+    g32 = eao.bwd_ext(tq, tk, tv, o, tdo, lse, causal=causal, window=150, alibi_slopes=ts, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = VA.backward(q, k, v, do, causal, 1.0 / np.sqrt(128), window=150, slopes=sl)
+    for a, b, r in zip(g32, g16, ref):
+        assert a.dtype == torch.float32
+        assert torch.equal(a.to(torch.bfloat16), b)
+        assert np.abs(f64(a) - r).max() <= TOL_G["bf16"]

@@ -108,3 +108,22 @@ def test_varlen_bwd_packed_workload():
         rq, rk, rv = VL.backward(sl(q), sl(k), sl(v), sl(do), np.array([0, s1 - s0]), True, 1.0 / np.sqrt(128))
         for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
             assert np.abs(got[:2, s0:s1] - ref).max() <= TOL_G["bf16"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_bwd_float32_gradients(causal):
+    """grad_dtype=float32: within the bar, and the stored bf16 gradients are these rounded."""
+    lens = [300, 0, 129, 77]
+    q, k, v, do, cu = _inputs(lens, 8, 2, 128, "bf16", seed=41)
+    dev = device()
+    tq, tk, tv, tdo = (to_dev(x, dev) for x in (q, k, v, do))
+    tcu = torch.from_numpy(cu).to(dev)
+    o, lse = eao.fwd_varlen(tq, tk, tv, tcu, 300, causal=causal)
+    g16 = eao.bwd_varlen(tq, tk, tv, o, tdo, lse, tcu, 300, causal=causal)
+    g32 = eao.bwd_varlen(tq, tk, tv, o, tdo, lse, tcu, 300, causal=causal, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = VL.backward(q, k, v, do, cu, causal, 1.0 / np.sqrt(128))
+    for a, b, r in zip(g32, g16, ref):
+        assert a.dtype == torch.float32
+        assert torch.equal(a.to(torch.bfloat16), b)
+        assert np.abs(f64(a) - r).max() <= TOL_G["bf16"]
