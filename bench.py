@@ -15,8 +15,8 @@ Besides the headline value it carries:
   * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same workload;
   * errors: the GPU's outputs of the sampled K/V head groups against the oracle's (max-abs,
     tolerances, pass); the run exits non-zero when a tolerance is missed;
-  * clock: the mean graphics clock during the timed steps and the fraction of the dense bf16 peak
-    at that clock.
+  * clock: the mean engine clock while the timed steps run (a probe kernel beside the same steps
+    repeated right after the timed region) and the fraction of the dense bf16 peak at that clock.
 """
 from __future__ import annotations
 
@@ -147,78 +147,36 @@ def check_results(w, gpu, outs):
                         f"{sorted(h for g in outs for h in range(g * G, (g + 1) * G))}), last timed step"}
 
 
-class ClockSampler:
-    """Samples the GPU's current graphics clock (amdsmi GPU metrics, mean over the XCDs) from a
-    host thread while the timed steps run; reports the mean over the samples."""
+def clock_window(step, steps, ms_total):
+    """Engine clock while the timed steps run: the same `steps` steps are run again (untimed)
+    with attn_clock_probe on a second stream beside them, one sleeping single-wave workgroup per
+    XCD for the length of the timed region.  A probe inside the timed region itself would hold a
+    wave slot on 8 compute units, which kernels at 256 registers per wave cannot share."""
+    import torch
 
-    def __init__(self, torch_device_index=0):
-        import threading
+    import exact_attention_online_amd as eao
 
-        self.samples, self.note = [], None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros(16, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    eao.clock_probe(out, max(1, int(ms_total * 1e5)), stream=side)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    cyc = out.view(8, 2).double().cpu()
+    ghz = (0.1 * cyc[:, 0] / cyc[:, 1]).tolist()
+    return sum(ghz) / len(ghz), ghz
 
-            amdsmi.amdsmi_init()
-            props = torch.cuda.get_device_properties(torch_device_index)
-            handles = amdsmi.amdsmi_get_processor_handles()
-            self._h = handles[0]
-            for h in handles:
-                bdf = str(amdsmi.amdsmi_get_gpu_device_bdf(h))
-                if int(bdf.split(":")[1], 16) == int(getattr(props, "pci_bus_id", -1)):
-                    self._h = h
-                    break
-            self._amdsmi = amdsmi
-            self._read()
-        except Exception as e:  # pragma: no cover - depends on the machine
-            self._h, self.note = None, f"GPU clock unavailable: {type(e).__name__}: {e}"
 
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
-        vals = m.get("current_gfxclks")
-        if isinstance(vals, (list, tuple)):
-            vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 65535]
-        if not vals:
-            x = m.get("current_gfxclk")
-            vals = [float(x)] if isinstance(x, (int, float)) and 0 < x < 65535 else []
-        if not vals:
-            raise RuntimeError("no graphics clock in the GPU metrics")
-        return sum(vals) / len(vals)
-
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception as e:  # pragma: no cover
-                self.note = f"GPU clock read failed: {e}"
-                return
-            time.sleep(0.001)
-
-    def start(self):
-        import threading
-
-        if self._h is not None:
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-            self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-
-    def result(self, rates):
-        """{mean GHz, samples, fraction of the dense peak at that clock for each named rate
-        (TFLOP/s)} or a note."""
-        if not self.samples:
-            return {"ghz": None, "note": self.note or "no samples"}
-        ghz = sum(self.samples) / len(self.samples) / 1000.0
-        peak = 256 * 4096 * ghz / 1000.0          # dense bf16 MFMA flop/clk of the chip x clock
-        return {"ghz": round(ghz, 3), "samples": len(self.samples), "peak_at_clock_tflops": round(peak, 1),
-                "frac_of_peak_at_clock": {k: round(v / peak, 4) for k, v in rates.items()},
-                "source": "amdsmi GPU metrics current_gfxclks, mean over XCDs and samples taken every ~1 ms "
-                          "from a host thread during the timed steps"}
+def clock_record(ghz, per_xcd, rates):
+    """{mean GHz, per-XCD GHz, fraction of the dense bf16 peak at that clock for each named rate}."""
+    peak = 256 * 4096 * ghz / 1000.0          # dense bf16 MFMA flop/clk of the chip x clock
+    return {"ghz": round(ghz, 3), "per_xcd_ghz": [round(x, 3) for x in per_xcd],
+            "peak_at_clock_tflops": round(peak, 1),
+            "frac_of_peak_at_clock": {k: round(v / peak, 4) for k, v in rates.items()},
+            "source": "attn_clock_probe (engine clocks / 100 MHz real-time ticks, one workgroup per XCD) on a "
+                      "second stream while the timed steps are repeated right after the timed region"}
 
 
 def cpu_baseline_decode(w, q, k, v, target_s):
@@ -541,9 +499,9 @@ def bench_ablation(args):
 
 
 def bench_fp8(args):
-    """FP8 forward (B=4, H=16, N=4096, d=128, non-causal, e4m3 with per-128-row scales): TFLOP/s of
-    attn_fwd on prepared codes, against the dense fp8 MFMA peak; the preparation (Hadamard +
-    quantisation, HBM-bound) is timed separately and not counted."""
+    """FP8 forward (B=4, H=16, N=4096, d=128, non-causal, e4m3 with per-128-row scales, V's rounded
+    up to powers of two): TFLOP/s of attn_fwd on prepared codes, against the dense fp8 MFMA peak;
+    the preparation (Hadamard + quantisation, HBM-bound) is timed separately and not counted."""
     import torch
 
     import exact_attention_online_amd as eao
@@ -560,7 +518,7 @@ def bench_fp8(args):
     ts = torch.from_numpy(signs).to(dev)
 
     def prep():
-        return (eao.fp8_prep(tq, ts), eao.fp8_prep(tk, ts), eao.fp8_prep(tv, None))
+        return (eao.fp8_prep(tq, ts), eao.fp8_prep(tk, ts), eao.fp8_prep(tv, None, pow2_scale=True))
 
     (q8, qs), (k8, ks), (v8, vs) = prep()
     o = torch.empty(w.B, w.Hq, w.N, w.d, dtype=torch.bfloat16, device=dev)
@@ -605,7 +563,7 @@ def bench_fp8(args):
         "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": f"fp8: B={w.B} H={w.Hq} N={w.N} d={w.d} non-causal, 0.1% outliers x10, e4m3 per "
-                               f"128 rows, Hadamard on Q and K", "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d,
+                               f"128 rows (V scales powers of two), Hadamard on Q and K", "B": w.B, "Hq": w.Hq, "N": w.N, "d": w.d,
                    "causal": w.causal, "seed": SEED, "pass": "fwd"},
         "prep_ms": round(ms_prep, 4),
         "prep_gbps": round(prep_bytes / (ms_prep * 1e-3) / 1e9, 1),
@@ -785,16 +743,14 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    clock = ClockSampler(dev.index or 0)
     torch.cuda.synchronize()
-    clock.start()
     t_start.record()
     for i in range(args.steps):
         step(evs[i])
     t_end.record()
     torch.cuda.synchronize()
-    clock.stop()
     total_ms = t_start.elapsed_time(t_end)
+    clk_ghz, clk_xcd = clock_window(step, args.steps, total_ms)
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dkdv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     dq_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
@@ -847,7 +803,8 @@ def main():
             "traffic": traffic,
         },
     }
-    out["clock"] = clock.result({"fwd+bwd": value, "fwd": f_fwd / (fwd_ms * 1e-3) / 1e12, "bwd_dkdv": dkdv_tflops})
+    out["clock"] = clock_record(clk_ghz, clk_xcd, {"fwd+bwd": value, "fwd": f_fwd / (fwd_ms * 1e-3) / 1e12,
+                                                    "bwd_dkdv": dkdv_tflops})
     failed = False
     if not args.no_cpu_baseline:
         out["cpu_baseline"], outs = cpu_baseline(w, qc, kc, vc, doc, args.cpu_seconds)

@@ -12,13 +12,13 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "attention", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
+    "fwd_splitkv", "splitkv_workspace_size", "attention", "clock_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
 ]
 
 F16, BF16, FP8_E4M3, F32 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
-           "attn_status_string")
+           "attn_clock_probe", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -68,8 +68,10 @@ def load():
     lib.attn_fwd_splitkv_workspace_size.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, sz, vp]
     lib.attn_fwd_splitkv.restype = i
-    lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 4 + [vp]
+    lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.attn_fp8_prep.restype = i
+    lib.attn_clock_probe.argtypes = [vp, i, ctypes.c_longlong, vp]
+    lib.attn_clock_probe.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -391,8 +393,9 @@ def bwd_phases(q, k, v, o, do, lse, causal, scale, workspace, dq, dk, dv, betwee
     return dq, dk, dv
 
 
-def fp8_prep(x, signs=None, out=None, descale=None):
-    """float32 x [B,H,N,d] -> (e4m3 codes as uint8 [B,H,N,d], float32 descale [B,H,ceil(N/128)])."""
+def fp8_prep(x, signs=None, out=None, descale=None, pow2_scale=False):
+    """float32 x [B,H,N,d] -> (e4m3 codes as uint8 [B,H,N,d], float32 descale [B,H,ceil(N/128)]);
+    pow2_scale: block scales rounded up to powers of two (what fwd_fp8 applies exactly to V)."""
     torch = _torch()
     if x.dim() != 4 or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise AttnError("x must be a contiguous float32 device tensor [B,H,N,d]")
@@ -408,7 +411,8 @@ def fp8_prep(x, signs=None, out=None, descale=None):
         _req(x.device, signs=(signs, (d,), torch.int8))
         sp = _ptr(signs)
     _req(x.device, out=(out, x.shape, torch.uint8), descale=(descale, (B, H, (N + 127) // 128), torch.float32))
-    _check(load().attn_fp8_prep(_ptr(x), _ptr(out), _ptr(descale), sp, B, H, N, d, _stream(x.device)))
+    _check(load().attn_fp8_prep(_ptr(x), _ptr(out), _ptr(descale), sp, B, H, N, d, int(bool(pow2_scale)),
+                                _stream(x.device)))
     return out, descale
 
 
@@ -435,6 +439,19 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool = False, s
     _check(load().attn_fwd(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
                            scale, FP8_E4M3, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _stream(q8.device)))
     return out, lse
+
+
+def clock_probe(out, ticks: int, stream=None):
+    """Launch attn_clock_probe: out is an int64 device tensor of 2 * groups entries (engine clocks
+    and 100 MHz real-time ticks per workgroup, filled when the probe ends); it runs on `stream`
+    (a torch.cuda.Stream, default: the current stream) for `ticks` real-time ticks.  Clock of
+    workgroup i in GHz: 0.1 * out[2i] / out[2i + 1]."""
+    torch = _torch()
+    if out.dtype != torch.int64 or out.dim() != 1 or out.numel() % 2 or not out.is_cuda or not out.is_contiguous():
+        raise AttnError("out must be a contiguous int64 device tensor of 2 * groups entries")
+    st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
+    _check(load().attn_clock_probe(_ptr(out), out.numel() // 2, int(ticks), ctypes.c_void_p(st)))
+    return out
 
 
 _AttentionFn = None

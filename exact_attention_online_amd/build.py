@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "fp8.hip", "splitkv.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "fp8.hip", "splitkv.hip", "clock.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -36,15 +36,16 @@ hipError_t launch_fwd_varlen(const void* q, const void* k, const void* v, void* 
                              int B, int Hq, int Hkv, int T, int max_seqlen, int d, bool causal, float scale,
                              bool bf16, hipStream_t stream);
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
-                           int d, hipStream_t stream);
+                           int d, bool pow2, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
                           const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N, int d,
                           bool causal, float scale, hipStream_t stream);
-size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, bool dense);
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                               int Hkv, int Nq, int Nk, int d, bool causal, float scale, bool bf16, int num_splits,
                               void* workspace, hipStream_t stream);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+hipError_t launch_clock_probe(unsigned long long* out, int groups, long long ticks, hipStream_t stream);
 }  // namespace eao
 
 namespace {
@@ -137,7 +138,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   if (check_sizes(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
-  return eao::bwd_workspace_bytes(B, Hq, Hkv, N, d);
+  return eao::bwd_workspace_bytes(B, Hq, Hkv, N, d, true);
 }
 
 // Shared checks of the backward entry points (pointer list, sizes, scale, dtype, workspace).
@@ -151,7 +152,7 @@ static int check_bwd(std::initializer_list<const void*> ptrs, int B, int Hq, int
   const int st = check_sizes(B, Hq, Hkv, N, d);
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
-  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, N, d, true)) return ATTN_ERR_WORKSPACE;
   return ATTN_OK;
 }
 
@@ -228,7 +229,7 @@ int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, con
 
 size_t attn_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int max_seqlen, int d) {
   if (check_sizes(B, Hq, Hkv, max_seqlen, d) != ATTN_OK) return 0;
-  return eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d);
+  return eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d, false);
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -247,7 +248,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   st = check_sizes(B, Hq, Hkv, max_seqlen, d);
   if (st != ATTN_OK) return st;
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return ATTN_ERR_WORKSPACE;
-  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < eao::bwd_workspace_bytes(B, Hq, Hkv, max_seqlen, d, false)) return ATTN_ERR_WORKSPACE;
   const bool bf16 = dtype == ATTN_BF16, out32 = grad_dtype == ATTN_F32;
   const hipStream_t s = (hipStream_t)stream;
   if (eao::launch_bwd_pre(q, k, o, dout, lse, B, Hq, Hkv, T, d, bf16, workspace, s, max_seqlen, cu_seqlens) !=
@@ -262,14 +263,16 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   return ATTN_OK;
 }
 
-// Shapes of the split-KV forward: the rows sharing one K/V head (Hq / Hkv heads x Nq rows) must
-// fit one 32-row MFMA tile.
+// Shapes of the split-KV forward: the rows sharing one K/V head (Hq / Hkv heads x Nq rows) are
+// taken in groups of 32; the grid (batch x K/V head x split x row group) must fit 32 bits.
 static int check_splitkv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
   if (Nq < 1 || Nk < 1 || num_splits < 0) return ATTN_ERR_INVALID;
   const int st = check_sizes(B, Hq, Hkv, Nk, d);
   if (st != ATTN_OK) return st;
   if (Nq > Nk) return ATTN_ERR_INVALID;
-  if ((Hq / Hkv) * Nq > 32) return ATTN_ERR_UNSUPPORTED;
+  if ((double)B * Hq * Nq * d > 9.0e15) return ATTN_ERR_INVALID;
+  const double row_groups = ((double)(Hq / Hkv) * Nq + 31.0) / 32.0;
+  if ((double)B * Hkv * row_groups * ((Nk + 127) / 128) > 2.0e9) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -293,13 +296,19 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_stream_t stream) {
+  if (out == nullptr || ((uintptr_t)out & 15u) != 0) return ATTN_ERR_INVALID;
+  if (groups < 1 || groups > 1024 || ticks < 1 || ticks > 1000000000LL) return ATTN_ERR_INVALID;
+  return eao::launch_clock_probe(out, groups, ticks, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs, int B, int H, int N, int d,
-                  attn_stream_t stream) {
+                  int pow2_scale, attn_stream_t stream) {
   if (!aligned16(x) || !aligned16(x_fp8) || !aligned16(descale)) return ATTN_ERR_INVALID;
   if (signs != nullptr && ((uintptr_t)signs & 15u) != 0) return ATTN_ERR_INVALID;
   const int st = check_sizes(B, H, H, N, d);
   if (st != ATTN_OK) return st;
-  const hipError_t e = eao::launch_fp8_prep(x, x_fp8, descale, signs, B, H, N, d, (hipStream_t)stream);
+  const hipError_t e = eao::launch_fp8_prep(x, x_fp8, descale, signs, B, H, N, d, pow2_scale != 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

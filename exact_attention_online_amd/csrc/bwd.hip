@@ -43,6 +43,7 @@
 //
 // Variants of the same kernels: VARLEN (sequences packed without padding, offsets from
 // cu_seqlens) and EXT (sliding window and ALiBi bias), described at the kernels.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -83,27 +84,46 @@ struct BwdWs {
   uint16_t* qt;
   uint16_t* dot;
   uint16_t* kt;
+  float* part;      // fp32 dK/dV shares of a split dK/dV phase (dkdv_splits > 1)
   int npad;
 };
 
-static BwdWs bwd_ws(void* workspace, int B, int Hq, int N, int d) {
+static BwdWs bwd_ws(void* workspace, int B, int Hq, int Hkv, int N, int d) {
   BwdWs w;
   w.npad = (N + kBwdRows - 1) / kBwdRows * kBwdRows;
   const size_t a = ((size_t)B * Hq * w.npad * 4 + 255) / 256 * 256;
   const size_t t = (size_t)B * Hq * w.npad * d * 2;
+  const size_t tk = (size_t)B * Hkv * w.npad * d * 2;
   char* base = (char*)workspace;
   w.dsum = (float*)base;
   w.lse2 = (float*)(base + a);
   w.qt = (uint16_t*)(base + 2 * a);
   w.dot = (uint16_t*)(base + 2 * a + t);
   w.kt = (uint16_t*)(base + 2 * a + 2 * t);
+  w.part = (float*)(base + 2 * a + 2 * t + tk);
   return w;
 }
 
-size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+// Splits of the dK/dV phase (dense layout).  The grid has one workgroup per (batch, K/V head,
+// block of 128 keys), each walking the G query heads of its group; with few K/V heads and a
+// short sequence it leaves most compute units idle.  Below one workgroup per CU the (query head,
+// query tile) steps of every key block are cut into up to 2G ranges (about two workgroups per
+// CU in all), each range's dK/dV share is kept in fp32 in the workspace and a second kernel adds
+// the shares in a fixed order: no atomics, deterministic.
+int dkdv_splits(int B, int Hq, int Hkv, int N) {
+  const int G = Hq / Hkv;
+  const long long wg = (long long)B * Hkv * ((N + kBwdKeys - 1) / kBwdKeys);
+  if (G < 2 || wg >= kNumCUs) return 1;
+  return (int)std::min<long long>((2 * kNumCUs + wg - 1) / wg, 2 * G);
+}
+
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, bool dense) {
   const size_t npad = (size_t)(N + kBwdRows - 1) / kBwdRows * kBwdRows;
   const size_t a = ((size_t)B * Hq * npad * 4 + 255) / 256 * 256;
-  return 2 * a + 2 * (size_t)B * Hq * npad * d * 2 + (size_t)B * Hkv * npad * d * 2;
+  size_t bytes = 2 * a + 2 * (size_t)B * Hq * npad * d * 2 + (size_t)B * Hkv * npad * d * 2;
+  const int ns = dense ? dkdv_splits(B, Hq, Hkv, N) : 1;
+  if (ns > 1) bytes += (size_t)ns * 2 * B * Hkv * N * d * 4;
+  return bytes;
 }
 
 // ------------------------------------------------------------------ 1. preprocess
@@ -274,7 +294,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, void* __restrict__ dK,
     void* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
-    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes, int out32) {
+    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes, int out32,
+    float* __restrict__ part, int nsplit) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = 8;                              // waves per workgroup
   constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
@@ -308,8 +329,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int G = Hq / Hkv;
   // key block major: under causal masking the first key blocks see the most query rows, so
   // the heaviest workgroups of every head start first
-  const int L = blockIdx.x;
-  const int BHkv = gridDim.x / nkb;
+  // split sp of nsplit of this key block's steps (adjacent workgroups, sharing the block's K and
+  // V in L2; nsplit = 1 except for small grouped-query grids, see dkdv_splits)
+  const int sp = (int)blockIdx.x % nsplit;
+  const int L = (int)blockIdx.x / nsplit;
+  const int BHkv = gridDim.x / (nkb * nsplit);
   // packed sequences: the same order, sequence by sequence (all blocks of sequence b's heads
   // before sequence b + 1), so that the workgroups in flight share their sequence's query tiles
   // in L2 as the workgroups of one batch do
@@ -360,6 +384,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   }
   const int per_head = qend - qstart;
   const int total = G * per_head;
+  // this workgroup's steps [it0, it1) of the block's G * per_head (query head, query tile) steps
+  const int it0 = (int)((long long)total * sp / nsplit);
+  const int it1 = (int)((long long)total * (sp + 1) / nsplit);
   // causal: only the first kBwdKeys / kBwdRows query blocks of every head cross the diagonal
   constexpr int kDiag = kBwdKeys / kBwdRows;
 
@@ -388,7 +415,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // Loader state: the block that the next call of load_next fetches (query head ld_hh of the
   // group, rows ld_q0 ..), and buffer descriptors over that head's Q, dO, transposed tiles and
   // statistics, rebuilt only when the head changes.
-  int ld_hh = 0, ld_q0 = qstart * kBwdRows, ld_left = per_head;
+  const int it0_tile = per_head > 0 ? it0 % per_head : 0;
+  int ld_hh = per_head > 0 ? min(it0 / per_head, G - 1) : 0;
+  int ld_q0 = (qstart + it0_tile) * kBwdRows, ld_left = per_head - it0_tile;
   __amdgpu_buffer_rsrc_t qrs, ors, qtrs, otrs, srs;
   auto head_rsrcs = [&]() __attribute__((always_inline)) {
     const size_t bhq = (size_t)b * Hq + kvh * G + ld_hh;
@@ -561,13 +590,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     __syncthreads();
   };
 
-  if (total > 0) load_next(Par0{});
+  if (it1 > it0) load_next(Par0{});
   wait_all_loads();
   __syncthreads();
-  int it = 0;
-  // unmasked steps [it, end) with the buffer parity of each step fixed at compile time
+  int it = it0;
+  // unmasked steps [it, end) with the buffer parity of each step (step it0 in buffer 0) fixed at
+  // compile time
   auto run = [&](int end) __attribute__((always_inline)) {
-    if ((it & 1) && it < end) {
+    if (((it - it0) & 1) && it < end) {
       step(0, 0.f, Par1{}, std::false_type{});
       ++it;
     }
@@ -606,24 +636,58 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       }
     }
   } else if constexpr (CAUSAL) {
-    for (int hh = 0; hh < G; ++hh) {
+    for (int hh = per_head > 0 ? it0 / per_head : G; it < it1; ++hh) {
       const int base = hh * per_head;
-      const int diag_end = min(base + kDiag, base + per_head);
+      const int diag_end = min(min(base + kDiag, base + per_head), it1);
       for (; it < diag_end; ++it) {
         const int q0 = (qstart + it - base) * kBwdRows;
-        if (it & 1) step(q0, 0.f, Par1{}, std::true_type{});
+        if ((it - it0) & 1) step(q0, 0.f, Par1{}, std::true_type{});
         else step(q0, 0.f, Par0{}, std::true_type{});
       }
-      run(base + per_head);
+      run(min(base + per_head, it1));
     }
   } else {
-    run(total);
+    run(it1);
   }
 
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
   const int key = kw + l32;
   if (key < N) {
-    store_row<BF16, DB>(role == 0 ? dV : dK, kv_off + (size_t)key * D, acc, role == 0 ? 1.f : scale, g, out32);
+    const float f = role == 0 ? 1.f : scale;
+    if (part != nullptr) {
+      // split: this workgroup's share in fp32, [split][dV, dK][B * Hkv * N][D]; summed in a
+      // fixed order by bwd_dkdv_sum_kernel
+      const size_t plane = (size_t)BHkv * N * D;
+      store_row<BF16, DB>(part + (2 * (size_t)sp + role) * plane, kv_off + (size_t)key * D, acc, f, g, 1);
+    } else {
+      store_row<BF16, DB>(role == 0 ? dV : dK, kv_off + (size_t)key * D, acc, f, g, out32);
+    }
+  }
+}
+
+// dK, dV = the sum of the nsplit fp32 shares [split][dV, dK][n] (n = B * Hkv * N * D), added in
+// split order (deterministic), stored as float (out32) or rounded to the input type.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restrict__ part, void* __restrict__ dK,
+                                                           void* __restrict__ dV, size_t n4, int nsplit, int out32) {
+  const float4* p4 = (const float4*)part;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n4; i += (size_t)gridDim.x * 256) {
+    const int role = i >= n4 ? 1 : 0;
+    const size_t j = i - (size_t)role * n4;
+    float4 a = p4[(size_t)role * n4 + j];
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 b = p4[(2 * (size_t)s + role) * n4 + j];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    void* out = role == 0 ? dV : dK;
+    if (out32) {
+      ((float4*)out)[j] = a;
+    } else {
+      ((uint2*)out)[j] = uint2{pack2<BF16>(a.x, a.y), pack2<BF16>(a.z, a.w)};
+    }
   }
 }
 
@@ -928,7 +992,7 @@ template <bool BF16, int D, bool VARLEN>
 static hipError_t launch_pre_t(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
                                int Hq, int Hkv, int N, int max_seqlen, const int* cu, void* workspace,
                                hipStream_t stream) {
-  const BwdWs w = bwd_ws(workspace, B, Hq, VARLEN ? max_seqlen : N, D);
+  const BwdWs w = bwd_ws(workspace, B, Hq, Hkv, VARLEN ? max_seqlen : N, D);
   const int ntile = w.npad / kBwdRows;
   const int nq_blocks = B * Hq * ntile;
   const unsigned grid = (unsigned)(nq_blocks + B * Hkv * ntile);
@@ -945,12 +1009,19 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
                                 const float* slopes = nullptr) {
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
   const int rows = VARLEN ? max_seqlen : N;
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, Hkv, rows, D);
   const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.dsum,
-                     w.lse2, w.qt, w.dot, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
-                     slopes, (int)out32);
+  const int ns = (VARLEN || EXT) ? 1 : dkdv_splits(B, Hq, Hkv, N);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv * ns), dim3(512), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                     w.dsum, w.lse2, w.qt, w.dot, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
+                     slopes, (int)out32, ns > 1 ? w.part : (float*)nullptr, ns);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  const size_t n4 = (size_t)B * Hkv * N * D / 4;
+  const unsigned grid = (unsigned)std::min<size_t>((2 * n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL((bwd_dkdv_sum_kernel<BF16>), dim3(grid), dim3(256), 0, stream, (const float*)w.part, dk, dv, n4,
+                     ns, (int)out32);
   return hipGetLastError();
 }
 
@@ -961,7 +1032,7 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
                               const float* slopes = nullptr) {
   (void)lse;
   const int rows = VARLEN ? max_seqlen : N;
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows, D);
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, Hkv, rows, D);
   const int BH = B * Hq;
   // 128-row blocks (4 waves) when 256-row blocks would give the CUs fewer than two workgroups
   // each (plain dense layout only); a row's arithmetic is the same either way

@@ -13,17 +13,19 @@
 //     h >= 8 across lanes (shuffles), exactly in the order of the definition so the codes are
 //     reproducible bit for bit; then a workgroup max of |y|, scale = amax / 448, and
 //     v_cvt_pk_fp8_f32 (round to nearest even) of y / scale.  HBM-bound: 4 bytes in, 1 out.
-//   * fwd_fp8_kernel: the forward of fwd.hip on v_mfma_scale_f32_32x32x64_f8f6f4 (scales 1).
-//     S^T = K Q^T with the descales folded into the exp2 argument (one scalar per tile pair).
-//     P~ in [0, 1] is multiplied by 2^8 before its e4m3 conversion (keeps small probabilities
-//     out of the subnormal range) and O^T += V^T P^T runs in fp8 as well.  The accumulator is
-//     kept in units of the current V block's scale: when the V block changes, the usual
-//     rescale factor exp(m_old - m_new) is multiplied by vscale_old / vscale_new, so block
-//     scales cost nothing extra; the epilogue multiplies by vscale * 2^-8 / l.
+//   * fwd_fp8_kernel: the forward of fwd.hip (same grid, direct loads, K one tile ahead of V,
+//     deferred rescaling) on v_mfma_scale_f32_32x32x64_f8f6f4 (scales 1).  S^T = K Q^T with the
+//     Q and K descales folded into the exp2 argument (one scalar per tile pair); the V block
+//     scale is folded into the exponent too (relative to the head's largest V scale), so the
+//     accumulator never needs rescaling when the V block changes.  The probabilities are
+//     multiplied by 2^7 before their e4m3 conversion (keeps small probabilities out of the
+//     subnormal range) and O^T += V^T P^T runs in fp8 as well.
 //     K rows are placed in LDS in a permuted order inside each 32-row block (row 8a + 4g + i
 //     holds key 16(a/2) + 8g + 4(a%2) + i), so each lane's accumulator registers cover runs of
 //     8 consecutive keys; ds_read_b64_tr_b8 on the naturally ordered V tile then yields V^T
 //     fragments whose k slots match.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace eao {
@@ -35,7 +37,17 @@ typedef i32x2_t __attribute__((address_space(3))) lds_i32x2_t;
 constexpr int kQBlock = 128;   // rows per quantisation block
 
 // ------------------------------------------------------------------ prep
-template <int D, bool HAD>
+// Block scale rounded up to a power of two: the smallest p = 2^e with 448 p >= amax.  With
+// amax = m 2^k, m in [1, 2): amax / 448 = (m / 1.75) 2^(k - 8), so e = k - 8, plus one when
+// m > 1.75; e is kept at or above -149 (the smallest float32).
+__device__ __forceinline__ float pow2_block_scale(float amax) {
+  int ex;
+  const float fr = frexpf(amax, &ex);        // amax = fr 2^ex, fr in [0.5, 1)
+  const int e = max(ex - 1 - 8 + (2.f * fr > 1.75f ? 1 : 0), -149);
+  return ldexpf(1.f, e);
+}
+
+template <int D, bool HAD, bool POW2>
 __global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
                                                        float* __restrict__ descale, const int8_t* __restrict__ signs,
                                                        int N, int nblk, float inv_sqrt_d) {
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  const float scale = amax > 0.f ? (POW2 ? pow2_block_scale(amax) : amax / 448.f) : 1.f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP + rloc;
@@ -112,17 +124,24 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__
   if (tid == 0) descale[(size_t)bh * nblk + qb] = scale;
 }
 
+template <int D, bool HAD>
+static void launch_prep_t(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int N, int nblk, float inv,
+                          bool pow2, dim3 grid, hipStream_t stream) {
+  if (pow2) hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, true>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
+  else hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, false>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
+}
+
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
-                           int d, hipStream_t stream) {
+                           int d, bool pow2, hipStream_t stream) {
   const int nblk = (N + kQBlock - 1) / kQBlock;
   const dim3 grid((unsigned)(B * H * nblk));
   const float inv = (float)(1.0 / sqrt((double)d));
   if (d == 128) {
-    if (signs) hipLaunchKernelGGL((fp8_prep_kernel<128, true>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
-    else hipLaunchKernelGGL((fp8_prep_kernel<128, false>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
+    if (signs) launch_prep_t<128, true>(x, x8, descale, signs, N, nblk, inv, pow2, grid, stream);
+    else launch_prep_t<128, false>(x, x8, descale, signs, N, nblk, inv, pow2, grid, stream);
   } else {
-    if (signs) hipLaunchKernelGGL((fp8_prep_kernel<64, true>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
-    else hipLaunchKernelGGL((fp8_prep_kernel<64, false>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
+    if (signs) launch_prep_t<64, true>(x, x8, descale, signs, N, nblk, inv, pow2, grid, stream);
+    else launch_prep_t<64, false>(x, x8, descale, signs, N, nblk, inv, pow2, grid, stream);
   }
   return hipGetLastError();
 }
@@ -132,10 +151,22 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
   // cbsz = blgp = 0: both operands fp8 e4m3; scale operands 127 = 2^0 (unscaled)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same with the A operand scaled by 2^(sa - 127) (an E8M0 exponent, 0 <= sa <= 254, the same
+// in every lane): the product is exact, as for any power of two.
+__device__ __forceinline__ f32x16_t mfma_fp8_sa(const i32x8_t& a, const i32x8_t& b, f32x16_t c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+}
 
-// Index (bytes) of byte `col` of row `row` in a tile of 128-byte rows, 16-byte chunks XOR-swizzled.
+// Index (bytes) of byte `col` of row `row` in a V tile of 128-byte rows, 16-byte chunks
+// XOR-swizzled by row % 8: the transposed 8-byte reads of 8 consecutive rows x 2 chunks hit 16
+// distinct 16-byte bank groups.
 __device__ __forceinline__ int fp8_index(int row, int col) {
   return row * 128 + ((((col >> 4) ^ (row & 7))) << 4) + (col & 15);
+}
+// The same for a K tile, swizzled by (row / 2) % 8: a 16-byte read of 16 consecutive rows at one
+// logical chunk hits 16 distinct bank groups (rows r and r + 8 share banks otherwise).
+__device__ __forceinline__ int fp8_index_k(int row, int col) {
+  return row * 128 + ((((col >> 4) ^ ((row >> 1) & 7))) << 4) + (col & 15);
 }
 
 // Key held by LDS row `rho` of a permuted 32-row K block (see the file comment).
@@ -144,31 +175,80 @@ __device__ __forceinline__ int fp8_key_of_row(int rho) {
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + i;
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
+// Headroom (log2 units) of the deferred rescaling: a row keeps its maximum until a score
+// passes it by more than this, so the probabilities against the kept maximum stay <= 2^1.
+constexpr float kFp8Stale = 1.0f;
+// log2 of the factor applied to the probabilities before their e4m3 conversion: probabilities
+// <= 2^kFp8Stale then map to <= 2^8 (e4m3 holds up to 448), and values down to 2^-13 of the kept
+// maximum stay in the normal range (e4m3 normals start at 2^-6).
+constexpr float kFp8Pre = 7.0f;
+// four e4m3 ones (sign 0, exponent 7 = bias, mantissa 0) packed in a 32-bit operand word
+constexpr int kFp8Ones = 0x38383838;
+
+// One workgroup per (batch, query head, block of NWV * 32 query rows), 32 rows per wave: 8 waves
+// (256 rows) when that gives every CU two or more workgroups, else 4.  Structure of
+// attn_fwd_kernel (fwd.hip): K and V tiles of 64 keys go straight from HBM into double-buffered
+// LDS with direct loads, K one tile ahead of V, and the S^T MFMAs of tile j + 1 share a basic
+// block with the exponentials and P V MFMAs of tile j.
+//
+// Scales.  S^T = K Q^T is in code units; ceff = scale * log2(e) * qscale * kscale of the tile's
+// 128-key block multiplies it inside the exponent.  The probabilities are formed against a row
+// maximum kept until a score passes it by more than kFp8Stale (rescaling on growth, as in
+// attn_fwd_kernel), times 2^kFp8Pre, and converted to e4m3; they carry no block scale, so the
+// largest ones stay exact.  The accumulator is kept in a unit u (a V block scale): a block whose
+// scale is u times a power of two (power-of-two block scales, attn_fp8_prep's pow2_scale) enters
+// through the A-operand scale of its P V MFMAs, exactly and without vector work; otherwise, at
+// the block's first tile, the accumulator is multiplied by u / vscale (with the rescale factor of
+// a grown maximum, if any) and u becomes that block's scale.  The row sums come from one more
+// MFMA per tile against an all-ones operand, i.e. over the same e4m3 probabilities that enter
+// the accumulator.  The per-tile scales are read one tile ahead with uniform (scalar) loads.
+// Epilogue: O = acc * u * 2^-kFp8Pre / l, LSE = ln 2 * (m + log2 l).
+template <bool CAUSAL, int NWV>
+__global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ qsc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, int Hq, int Hkv, int N, int BH, int nqb, int nblk, float c) {
-  constexpr int D = 128, BC = 64, BR = 128;
+  constexpr int D = 128, BC = 64, BR = NWV * 32;
   constexpr int TILE = BC * D;                 // bytes per K or V tile
-  extern __shared__ uint4 smem_fp8[];
-  uint8_t* sm = (uint8_t*)smem_fp8;            // [buf][K, V] tiles of TILE bytes
+  constexpr int PIECES = TILE / 1024;          // 1 KB direct-load pieces per tile
+  static_assert(PIECES % NWV == 0, "each wave moves the same number of pieces");
+  constexpr int PW = PIECES / NWV;
+  // four distinct LDS objects (see attn_fwd_kernel)
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE];
+  auto Ks = [&](auto par) -> uint8_t* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
+  };
+  auto Vs = [&](auto par) -> uint8_t* __attribute__((always_inline)) {
+    if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
+  };
+
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int G16 = lane >> 4, li = lane & 15;
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  // block order of attn_fwd_kernel: heads in chunks of 32 (when 32 divides B * Hq), all query
+  // blocks of a chunk before the next, causal launches longest blocks first
+  const int HC = (BH % 32 == 0) ? 32 : BH;
+  const int Lb = L % (HC * nqb);
+  const int qblk = CAUSAL ? (nqb - 1 - Lb / HC) : (Lb / HC);
+  const int bh = (L / (HC * nqb)) * HC + Lb % HC;
   const int h = bh % Hq, b = bh / Hq;
   const int kvh = h / (Hq / Hkv);
-  const size_t q_off = ((size_t)b * Hq + h) * (size_t)N * D;
-  const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)N * D;
+  const int bkv = b * Hkv + kvh;
+  const size_t q_off = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)bkv * N * D;
   const int q0 = qblk * BR;
   const int qw = q0 + 32 * w;
+  const int qw_last = qw + 31;
   const int qrow = qw + l32;
-  const float qs_val = qsc[((size_t)b * Hq + h) * nblk + qblk];   // BR == quantisation block
-  const float* ks_head = ksc + ((size_t)b * Hkv + kvh) * nblk;
-  const float* vs_head = vsc + ((size_t)b * Hkv + kvh) * nblk;
+  // the wave's 32 rows lie in one 128-row quantisation block
+  const float qs_val = qsc[(size_t)bh * nblk + min(qw / kQBlock, nblk - 1)];
+  const float* ks_head = ksc + (size_t)bkv * nblk;
+  const float* vs_head = vsc + (size_t)bkv * nblk;
+  const float cq = c * qs_val;
 
   // Q^T fragments: lane holds Q[qrow][64kk + 32g .. +31]
   i32x8_t qf[2];
@@ -182,135 +262,222 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
       qf[kk] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  wait_all_loads();
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-  float m = -INFINITY, l = 0.f, vs_cur = 1.f;
+  // row sums of the e4m3 probabilities, from one more MFMA per tile with an all-ones A operand
+  // (every register of a lane ends up holding its query's sum): the sum costs no vector ALU work
+  f32x16_t lacc = f32x16_t{};
+  const i32x8_t ones = {kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
+  float m = -INFINITY;
+  float vs_cur = vs_head[0];   // the accumulator's unit: the V scale of the last block added
 
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
-  // staging: 2 chunks of 16 bytes per thread for each of K and V (64 rows x 8 chunks)
-  uint4 kreg[2], vreg[2];
-  auto load_tile = [&](int kt0) {
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, (uint32_t)N * D);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, (uint32_t)N * D);
+  // direct loads: piece p = NWV i + w of a tile covers LDS rows 8p .. 8p + 7; lane l fills row
+  // 8p + l / 8, physical chunk l % 8 with the logical chunk the swizzle puts there, from the key
+  // that row holds (K rows permuted inside each 32-row block, V rows in order)
+  uint32_t goff_k[PW], goff_v[PW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cidx = tid + 256 * i;
-      const int rho = cidx >> 3, ch = cidx & 7;
-      const int kkey = kt0 + (rho & ~31) + fp8_key_of_row(rho & 31);
-      const int vkey = kt0 + rho;
-      kreg[i] = kkey < N ? *(const uint4*)(K + kv_off + (size_t)kkey * D + 16 * ch) : uint4{0, 0, 0, 0};
-      vreg[i] = vkey < N ? *(const uint4*)(V + kv_off + (size_t)vkey * D + 16 * ch) : uint4{0, 0, 0, 0};
+  for (int i = 0; i < PW; ++i) {
+    const int row = 8 * (NWV * i + w) + (lane >> 3);
+    const int lc = (lane & 7) ^ (row & 7);
+    const int lck = (lane & 7) ^ ((row >> 1) & 7);
+    goff_k[i] = (uint32_t)((row & ~31) + fp8_key_of_row(row & 31)) * D + 16 * lck;
+    goff_v[i] = (uint32_t)row * D + 16 * lc;
+  }
+  auto load_k = [&](uint8_t* dst, int kt0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      buffer_load16_lds(krs, (short*)(dst + 1024 * (NWV * i + w)), goff_k[i] + (uint32_t)kt0 * D);
+  };
+  auto load_v = [&](uint8_t* dst, int kt0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      buffer_load16_lds(vrs, (short*)(dst + 1024 * (NWV * i + w)), goff_v[i] + (uint32_t)kt0 * D);
+  };
+
+  // loop-invariant LDS read offsets (bytes): K rows l32 (+32 kb: the swizzle repeats every 16
+  // rows) at byte columns 64kk + 32g (+16);
+  // V^T transposed reads at rows 8(G16/2) + li/2 (+16t), columns 32db + 16(G16%2) + 8(li%2)
+  int off_k[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) off_k[kk][hh] = fp8_index_k(l32, 64 * kk + 32 * g + 16 * hh);
+  int off_v[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) off_v[db] = fp8_index(8 * (G16 >> 1) + (li >> 1), 32 * db + 16 * (G16 & 1) + 8 * (li & 1));
+
+  // a wave takes part in tiles [0, jact); causal: tiles after its last row are skipped (it still
+  // helps stage them)
+  const int jact = (qw >= N) ? 0 : (CAUSAL ? min(ntiles, qw_last / BC + 1) : ntiles);
+
+  // S^T = K Q^T for the key tile in K buffer `par`
+  auto compute_s = [&](auto par, f32x16_t (&s)[2]) __attribute__((always_inline)) {
+    const uint8_t* Kb = Ks(par);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint4 x0 = *(const uint4*)(Kb + 32 * kb * D + off_k[kk][0]);
+        const uint4 x1 = *(const uint4*)(Kb + 32 * kb * D + off_k[kk][1]);
+        const i32x8_t a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        s[kb] = mfma_fp8(a, qf[kk], s[kb]);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cidx = tid + 256 * i;
-      const int rho = cidx >> 3, ch = cidx & 7;
-      *(uint4*)(sm + buf * 2 * TILE + fp8_index(rho, 16 * ch)) = kreg[i];
-      *(uint4*)(sm + buf * 2 * TILE + TILE + fp8_index(rho, 16 * ch)) = vreg[i];
-    }
+  // staging of one iteration (tile j lives in the buffers of parity j % 2): K_{j+2} replaces
+  // K_j, V_{j+1} replaces V_{j-1}
+  auto stage = [&](int j, auto par) __attribute__((always_inline)) {
+    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
+    if (j + 2 < ntiles) load_k(Ks(par), (j + 2) * BC);
+    if (j + 1 < ntiles) load_v(Vs(Other{}), (j + 1) * BC);
   };
-  load_tile(0);
-  store_tile(0);
+  auto publish = [&]() __attribute__((always_inline)) {
+    wait_all_loads();
+    __syncthreads();
+  };
+
+  f32x16_t sA[2], sB[2];   // S^T of even / odd tiles
+  // scales of tile j's 128-key block (uniform): kscale folded into ceff, and the V scale; sa:
+  // E8M0 scale of the P V MFMAs of the current V block (127 = 2^0)
+  float ceff = cq * ks_head[0], vs_t = vs_cur;
+  int sa = 127;
+  // BSTART: the tile starts a 128-key block (tiles are 64 keys: even tiles)
+  auto body = [&](int j, auto par, auto mask_tag, auto bstart_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool BSTART = decltype(bstart_tag)::value;
+    constexpr int P = decltype(par)::value;
+    using Other = std::integral_constant<int, 1 - P>;
+    auto& sc = P == 0 ? sA : sB;
+    auto& sn = P == 0 ? sB : sA;
+    const int kt0 = j * BC;
+    stage(j, par);
+    // scales of the next tile, read now (scalar loads, used one iteration later)
+    const int jbn = __builtin_amdgcn_readfirstlane(min((kt0 + BC) / kQBlock, nblk - 1));
+    const float ks_n = ks_head[jbn], vs_n = vs_head[jbn];
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // register r holds key 32kb + 16(r/8) + 8g + r%8 of the tile
+          const int key = kt0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (key >= N || (CAUSAL && key > qrow)) sc[kb][r] = -INFINITY;
+        }
+    }
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[kb][r]);
+    const float mt = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * ceff;
+    // A new V block: when its scale is an exact power of two times the accumulator's unit
+    // (power-of-two block scales), the P V MFMAs apply that factor through their A-operand
+    // scale; otherwise the accumulator changes unit (vs_cur -> this block's scale).
+    bool vres = false;
+    if constexpr (BSTART) {
+      const uint32_t rb = __float_as_uint(vs_t / vs_cur);
+      const uint32_t ef = (rb >> 23) & 0xFFu;
+      if ((rb & 0x7FFFFFu) == 0u && ef >= 1u && ef <= 254u) {
+        sa = (int)ef;          // E8M0 exponent of the ratio
+      } else {
+        vres = true;
+        sa = 127;
+      }
+    }
+    // deferred rescale, per row, as in attn_fwd_kernel
+    const bool grow = mt > m + kFp8Stale;
+    const bool any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (vres || any_grow) {
+      float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+      asm volatile("" : "+v"(alpha));
+      m = grow ? mt : m;
+      const float f = vres ? alpha * (vs_cur / vs_t) : alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= f;
+      if (any_grow) lacc *= alpha;
+      if (vres) vs_cur = vs_t;
+    }
+    const float mo = ((m == -INFINITY) ? 0.f : m) - kFp8Pre;
+    // S^T of the next tile (past the wave's last tile it reads a stale buffer; never used)
+    compute_s(Other{}, sn);
+    int pw[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(sc[kb][r + e] * ceff - mo);
+        // the conversion keeps the other half of its "old" operand: old = p[0]'s dying register
+        // (both halves are overwritten here) spares a zeroed register
+        const int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
+        pw[(16 * kb + r) / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
+      }
+    // B operand (P^T): slot e = 16kb + r  ->  key 32kb + 16(r/8) + 8g + (r%8)
+    const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    lacc = mfma_fp8(ones, pb, lacc);
+    const uint8_t* Vb = Vs(par);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      int av[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // 8 consecutive keys 16t + 8g .. +7 at column d = 32db + l32
+        const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(Vb + 16 * t * D + off_v[db]));
+        av[2 * t] = x[0];
+        av[2 * t + 1] = x[1];
+      }
+      const i32x8_t a = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+      o[db] = mfma_fp8_sa(a, pb, o[db], sa);
+    }
+    ceff = cq * ks_n;
+    vs_t = vs_n;
+    publish();
+  };
+  auto idle = [&](int j) __attribute__((always_inline)) {
+    if (j & 1) stage(j, Par1{});
+    else stage(j, Par0{});
+    publish();
+  };
+
+  // prologue: K and V of tile 0, K of tile 1; S^T of tile 0
+  load_k(Ks(Par0{}), 0);
+  load_v(Vs(Par0{}), 0);
+  if (1 < ntiles) load_k(Ks(Par1{}), BC);
+  publish();
+  if (jact > 0) compute_s(Par0{}, sA);
+  // the first iteration overwrites the K buffer of tile 0
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kt0 = j * BC;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(kt0 + BC);
-    const bool active = (qw < N) && (!CAUSAL || kt0 <= qw + 31);
-    if (active) {
-      const uint8_t* Kb = sm + (j & 1) * 2 * TILE;
-      const uint8_t* Vb = Kb + TILE;
-      const float vs_new = vs_head[kt0 / kQBlock];
-      const float ceff = c * qs_val * ks_head[kt0 / kQBlock];
-      f32x16_t s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int row = 32 * kb + l32;
-          const uint4 x0 = *(const uint4*)(Kb + fp8_index(row, 64 * kk + 32 * g));
-          const uint4 x1 = *(const uint4*)(Kb + fp8_index(row, 64 * kk + 32 * g + 16));
-          const i32x8_t a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          s[kb] = mfma_fp8(a, qf[kk], s[kb]);
-        }
-      }
-      const bool need_mask = (kt0 + BC > N) || (CAUSAL && kt0 + BC - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + 32 * kb + fp8_key_of_row(8 * (r >> 2) + 4 * g + (r & 3));
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = max_halves(mx);
-      const float mnew = fmaxf(m, mx * ceff);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m - muse);
-      m = mnew;
-      // the probabilities come out pre-scaled by 2^8 (the exponent carries the + 8), so they
-      // convert to e4m3 as they are; l sums the same scaled values, which the final division
-      // cancels
-      const float muse8 = muse - 8.f;
-      float rs = 0.f;
-      int pw[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(s[kb][r + e] * ceff - muse8);
-            rs += p[e];
-          }
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pw[(16 * kb + r) / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
-        }
-      l = l * alpha + rs;
-      // accumulator is kept in units of the current V block's scale; the factor is exactly 1
-      // (and the multiplies are skipped) while neither the row maximum nor the V block changes
-      const float rescale = alpha * (vs_cur / vs_new);
-      vs_cur = vs_new;
-      if (__builtin_amdgcn_ballot_w64(rescale != 1.f) != 0) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= rescale;
-      }
-      // B operand (P^T): slot e = 16kb + r  ->  key 32kb + 16(r/8) + 8g + (r%8)
-      const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        int av[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // 8 consecutive keys 16t + 8g .. +7 at column d = 32db + l32
-          const int row = 16 * t + 8 * (G16 >> 1) + (li >> 1);
-          const int col = 32 * db + 16 * (G16 & 1) + 8 * (li & 1);
-          const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(Vb + fp8_index(row, col)));
-          av[2 * t] = x[0];
-          av[2 * t + 1] = x[1];
-        }
-        const i32x8_t a = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-        o[db] = mfma_fp8(a, pb, o[db]);
-      }
-    }
-    if (has_next) store_tile((j + 1) & 1);
-    __syncthreads();
+  // tiles [0, jmask) need no mask for any wave of the workgroup (before the diagonal of its
+  // first row and before the key tail); even tiles start a 128-key block
+  const int jmask = min(jact, CAUSAL ? min(q0, N) / BC : N / BC);
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = 0;
+  for (; j + 2 <= jmask; j += 2) {
+    body(j, Par0{}, F_{}, T_{});
+    body(j + 1, Par1{}, F_{}, F_{});
   }
+  if (j < jmask) {
+    body(j, Par0{}, F_{}, T_{});
+    ++j;
+  }
+  for (; j < jact; ++j) {
+    if (j & 1) body(j, Par1{}, T_{}, F_{});
+    else body(j, Par0{}, T_{}, T_{});
+  }
+  for (; j < ntiles; ++j) idle(j);
 
-  const float lt = sum_halves(l);                // 2^8 times the sum of the probabilities
-  const float fin = vs_cur / lt;
+  // l: the sum of the probabilities P~ = p * 2^-kFp8Pre that entered the accumulator
+  const float lt = lacc[0] * (1.f / (float)(1 << (int)kFp8Pre));
+  const float fin = vs_cur * (1.f / (float)(1 << (int)kFp8Pre)) / lt;
   if (qrow < N) {
     uint16_t* Op = O + q_off + (size_t)qrow * D;
 #pragma unroll
@@ -323,25 +490,34 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         pk.y = pack2<true>(o[db][4 * rr + 2] * fin, o[db][4 * rr + 3] * fin);
         *(uint2*)(Op + d0) = pk;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = (m - 8.f + __log2f(lt)) * kLn2;
+    if (g == 0) LSE[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
   }
+}
+
+template <bool CAUSAL, int NWV>
+static void launch_fwd_fp8_t(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
+                             const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N,
+                             float scale, hipStream_t stream) {
+  constexpr int BR = NWV * 32;
+  const int nqb = (N + BR - 1) / BR;
+  const int nblk = (N + kQBlock - 1) / kQBlock;
+  const int BH = B * Hq;
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, NWV>), dim3(nqb * BH), dim3(NWV * 64), 0, stream, q, k, v, o, lse, qs,
+                     ks, vs, Hq, Hkv, N, BH, nqb, nblk, scale * kLog2e);
 }
 
 hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, uint16_t* o, float* lse,
                           const float* qs, const float* ks, const float* vs, int B, int Hq, int Hkv, int N, int d,
                           bool causal, float scale, hipStream_t stream) {
   (void)d;  // only d = 128 is built (checked by the caller)
-  constexpr int BR = 128;
-  const int nqb = (N + BR - 1) / BR;
-  const int nblk = (N + kQBlock - 1) / kQBlock;
-  const int BH = B * Hq;
-  const size_t lds = 4 * 64 * 128;
+  // 256-row blocks when they give every CU at least two workgroups, else 128-row blocks
+  const bool big = (long long)B * Hq * ((N + 255) / 256) >= 2 * kNumCUs;
   if (causal) {
-    hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3(nqb * BH), dim3(256), lds, stream, q, k, v, o, lse, qs, ks, vs, Hq,
-                       Hkv, N, BH, nqb, nblk, scale * kLog2e);
+    if (big) launch_fwd_fp8_t<true, 8>(q, k, v, o, lse, qs, ks, vs, B, Hq, Hkv, N, scale, stream);
+    else launch_fwd_fp8_t<true, 4>(q, k, v, o, lse, qs, ks, vs, B, Hq, Hkv, N, scale, stream);
   } else {
-    hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3(nqb * BH), dim3(256), lds, stream, q, k, v, o, lse, qs, ks, vs, Hq,
-                       Hkv, N, BH, nqb, nblk, scale * kLog2e);
+    if (big) launch_fwd_fp8_t<false, 8>(q, k, v, o, lse, qs, ks, vs, B, Hq, Hkv, N, scale, stream);
+    else launch_fwd_fp8_t<false, 4>(q, k, v, o, lse, qs, ks, vs, B, Hq, Hkv, N, scale, stream);
   }
   return hipGetLastError();
 }

@@ -10,9 +10,11 @@
 //   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
 //
 // gfx950 mapping
-//   * split kernel: one workgroup of 4 waves per (batch, K/V head, split).  All query rows that
-//     use the K/V head -- G = Hq / Hkv heads times Nq rows, at most 32 -- form the 32 columns of
-//     one MFMA tile (transposed formulation as in the main forward: a lane owns one row).  Key
+//   * split kernel: one workgroup of 4 waves per (batch, K/V head, split, group of 32 rows).
+//     The query rows that use the K/V head -- G = Hq / Hkv heads times Nq rows -- are taken 32 at
+//     a time as the 32 columns of one MFMA tile (transposed formulation as in the main forward:
+//     a lane owns one row); the workgroups of one split's row groups are adjacent in the grid,
+//     so beyond the first they find the split's keys in L2.  Key
 //     tiles of 128 go straight from HBM into double-buffered LDS (direct buffer -> LDS loads);
 //     each wave takes its own 32 keys of every tile and keeps its own running max, sum and
 //     O^T, so the four waves stream disjoint keys and are merged once, through LDS, at the end.
@@ -27,14 +29,18 @@ namespace eao {
 
 constexpr int kSkTile = 128;   // keys per tile (32 per wave)
 
+// groups of 32 query rows per K/V head
+static int splitkv_row_groups(int Hq, int Hkv, int Nq) { return ((Hq / Hkv) * Nq + 31) / 32; }
+
 // keys per split (a multiple of the tile) and number of splits for a launch
-void splitkv_plan(int B, int Hkv, int Nk, int num_splits, int* splits, int* keys_per_split) {
+void splitkv_plan(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits, int* splits, int* keys_per_split) {
   const int tiles = (Nk + kSkTile - 1) / kSkTile;
   int s = num_splits;
   if (s <= 0) {
     // about two workgroups per compute unit, but splits of at least 8 tiles: shorter splits
     // spend more time in their prologue and the merge than they save
-    const int want = (2 * 256 + B * Hkv - 1) / (B * Hkv);
+    const int wg = B * Hkv * splitkv_row_groups(Hq, Hkv, Nq);
+    const int want = (2 * 256 + wg - 1) / wg;
     s = want < tiles / 8 ? want : tiles / 8;
   }
   s = s < 1 ? 1 : (s > tiles ? tiles : s);
@@ -45,7 +51,7 @@ void splitkv_plan(int B, int Hkv, int Nk, int num_splits, int* splits, int* keys
 
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
   int s, l;
-  splitkv_plan(B, Hkv, Nk, num_splits, &s, &l);
+  splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &s, &l);
   const size_t rows = (size_t)s * B * Hq * Nq;
   return (rows * d * 4 + 255) / 256 * 256 + (rows * 4 + 255) / 256 * 256;
 }
@@ -75,11 +81,12 @@ __global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int G16 = lane >> 4, li = lane & 15;
-  const int G = Hq / Hkv, R = G * Nq;
-  const int s = blockIdx.x % S, bkv = blockIdx.x / S;
+  const int G = Hq / Hkv, R = G * Nq, RG = (R + 31) / 32;
+  const int rg = blockIdx.x % RG, s = (blockIdx.x / RG) % S, bkv = blockIdx.x / (RG * S);
   const int b = bkv / Hkv, kvh = bkv % Hkv;
+  const int r0 = 32 * rg;                           // first row of this workgroup's group
   // this lane's query row: head kvh * G + row / Nq, row row % Nq (rows >= R are padding)
-  const int row = l32;
+  const int row = r0 + l32;
   const bool row_ok = row < R;
   const int gh = row_ok ? row / Nq : 0, qi = row_ok ? row % Nq : 0;
   const int hq = kvh * G + gh;
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __res
   const size_t prow0 = (size_t)s * B * Hq * Nq;      // partial rows of split s
   for (int e = tid; e < 32 * D; e += 256) {
     const int rr = e / D, d = e % D;
-    if (rr >= R) continue;
+    if (r0 + rr >= R) continue;
     float mtot = -INFINITY, ltot = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) mtot = fmaxf(mtot, red_m[ww][rr]);
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __res
       ltot += red_l[ww][rr] * f;
       sum += (ww < 2 ? ost_k : ost_v)[((ww & 1) * 32 + rr) * D + d];
     }
-    const int ghh = rr / Nq, qq = rr % Nq;
+    const int ghh = (r0 + rr) / Nq, qq = (r0 + rr) % Nq;
     const size_t prow = prow0 + ((size_t)b * Hq + kvh * G + ghh) * Nq + qq;
     Opart[prow * D + d] = ltot > 0.f ? sum / ltot : 0.f;
     if (d == 0) Lpart[prow] = ltot > 0.f ? (mtot + __log2f(ltot)) * kLn2 : -INFINITY;
@@ -287,11 +294,12 @@ static hipError_t launch_split_t(const void* q, const void* k, const void* v, vo
                                  int Hkv, int Nq, int Nk, float scale, int num_splits, void* workspace,
                                  hipStream_t stream) {
   int S, L;
-  splitkv_plan(B, Hkv, Nk, num_splits, &S, &L);
+  splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &S, &L);
   const size_t rows = (size_t)B * Hq * Nq;
+  const int RG = splitkv_row_groups(Hq, Hkv, Nq);
   float* opart = (float*)workspace;
   float* lpart = (float*)((char*)workspace + ((size_t)S * rows * D * 4 + 255) / 256 * 256);
-  hipLaunchKernelGGL((fwd_split_kernel<BF16, D, CAUSAL>), dim3((unsigned)(B * Hkv * S)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_split_kernel<BF16, D, CAUSAL>), dim3((unsigned)(B * Hkv * S * RG)), dim3(256), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, opart, lpart, B, Hq, Hkv, Nq, Nk,
                      S, L, scale * kLog2e);
   hipError_t e = hipGetLastError();

@@ -124,7 +124,9 @@ int attn_bwd_ext(const void* q, const void* k, const void* v, const void* o, con
  * without padding ("FlashAttention-2: Faster Attention with Better Parallelism and Work
  * Partitioning", OpenReview discussion, author responses: concatenated sequences and an array of
  * lengths; "FlashAttention (NeurIPS 2022)" notes, "Backward - Recomputation").  Each sequence's
- * gradients are those attn_bwd gives for that sequence alone.
+ * gradients are those attn_bwd gives for that sequence alone (dq bit for bit; dk and dv up to the
+ * order of their fp32 additions, since attn_bwd splits the dK/dV phase of small grouped problems
+ * and this entry point never does).
  *   q, o, dout [Hq,T,d], k, v [Hkv,T,d] in `dtype` (ATTN_F16 / ATTN_BF16), lse [Hq,T] float from
  *   attn_fwd_varlen with the same cu_seqlens, causal flag and scale; cu_seqlens, B, T and
  *   max_seqlen as for attn_fwd_varlen.  Outputs dq [Hq,T,d], dk, dv [Hkv,T,d] in `grad_dtype`
@@ -145,7 +147,10 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
  * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
  * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and
  * [B,Hkv,Npad,d] (K), i.e. 2 * roundup(4 * B * Hq * Npad, 256) + 2 * (2 * Hq + Hkv) * B * Npad * d
- * bytes.  0 if the sizes are invalid. */
+ * bytes.  Grouped-query problems (Hq > Hkv) whose B * Hkv * ceil(N / 128) is below 256 split the
+ * dK/dV phase S = min(ceil(512 / (B * Hkv * ceil(N / 128))), 2 * Hq / Hkv) ways, so that it fills
+ * the GPU, and add S * 2 * B * Hkv * N * d * 4 bytes for the float shares (added in a fixed
+ * order, so the gradients stay deterministic).  0 if the sizes are invalid. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 
 /* Backward pass of L = <O, dO> ("FlashAttention (NeurIPS 2022)" notes, "Backward -
@@ -197,8 +202,10 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
  * into splits processed by separate workgroups; each split's exact partial result and logsumexp
  * are combined by LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
  *   q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d]; o [B,Hq,Nq,d] in `dtype` (ATTN_F16 / ATTN_BF16);
- *   lse [B,Hq,Nq] float, natural log.  Requires 1 <= Nq <= Nk and (Hq/Hkv) * Nq <= 32 (all rows
- *   that share a K/V head fit one 32-row tile), else ATTN_ERR_UNSUPPORTED / ATTN_ERR_INVALID.
+ *   lse [B,Hq,Nq] float, natural log.  Requires 1 <= Nq <= Nk, else ATTN_ERR_INVALID.  The
+ *   (Hq/Hkv) * Nq rows that share a K/V head are processed 32 at a time (workgroups of one key
+ *   split and K/V head differ only in their group of 32 rows), so up to 32 rows per K/V head
+ *   stream the keys once and more rows re-read them mostly from the L2 cache.
  *   causal: query i sits at position Nk - Nq + i and sees keys j <= Nk - Nq + i (with Nq = 1
  *   every key is visible).
  *   num_splits: splits per (batch, K/V head), 0 = chosen for about two workgroups per compute
@@ -216,11 +223,25 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is
  * first replaced by (row * signs) H_d / sqrt(d), H_d the Sylvester Hadamard matrix, computed in
  * float32 with the butterfly stages in order h = 1, 2, ..., d/2.  Then for every block of 128
- * rows of a head: scale = amax / 448 (1 if amax == 0), codes = e4m3(x / scale) rounded to
- * nearest even and saturated to +-448.  Writes x_fp8 uint8 [B,H,N,d] and descale float
- * [B,H,ceil(N/128)] (= scale).  Returns an attn_status_t. */
+ * rows of a head: scale = amax / 448 (1 if amax == 0), or with pow2_scale != 0 the smallest power
+ * of two p with 448 p >= amax (1 if amax == 0); codes = e4m3(x / scale) rounded to nearest even
+ * and saturated to +-448.  Writes x_fp8 uint8 [B,H,N,d] and descale float [B,H,ceil(N/128)]
+ * (= scale).  attn_fwd applies power-of-two V scales exactly inside its matrix multiplies (the
+ * E8M0 block-scale operand of gfx950's fp8 MFMA), any other V scale by rescaling its
+ * accumulator; Q and K scales of either kind cost nothing extra.  Returns an attn_status_t. */
 int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs,
-                  int B, int H, int N, int d, attn_stream_t stream);
+                  int B, int H, int N, int d, int pow2_scale, attn_stream_t stream);
+
+/* Measurement aid, not a step of the attention method: the engine clock a workload ran at.
+ * Launches `groups` single-wave workgroups on `stream`; each reads the shader clock counter
+ * (one tick per engine clock) and the 100 MHz real-time counter, sleeps until `ticks` real-time
+ * ticks have passed, and writes out[2 i] = engine clocks elapsed, out[2 i + 1] = real-time ticks
+ * elapsed (uint64, device memory, 16-byte aligned).  Workgroup i starts on XCD i % 8 of an MI355X,
+ * so 8 groups sample every XCD; its clock is 100 MHz * out[2 i] / out[2 i + 1].  Launched on a
+ * second stream beside a workload it samples the clock that workload runs at; its waves mostly
+ * sleep but each holds a wave slot on one compute unit.  1 <= groups <= 1024 and
+ * 1 <= ticks <= 10^9 (10 s), else ATTN_ERR_INVALID.  Returns an attn_status_t. */
+int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_stream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char* attn_status_string(int status);

@@ -12,7 +12,10 @@ Readings where the page is silent (each also recorded in the design notes):
     Q K^T unchanged because M M^T = I), not to V;
   * one fp32 scale per (batch, head, block of 128 consecutive rows), scale = amax / 448
     (amax = largest magnitude in the block, all d columns; scale = 1 if amax = 0), and the
-    stored code is e4m3(x / scale);
+    stored code is e4m3(x / scale); or, as an option, the scale rounded up to a power of two:
+    the smallest p = 2^e with 448 p >= amax (the E8M0 form of a block scale, which a
+    block-scaled matrix multiply applies exactly; the page fixes one scale per block, not its
+    value);
   * precision: the transform and the division run in float32 (the precision in which the GPU
     takes the same rounding decisions), the butterfly in the standard stage order
     h = 1, 2, 4, ..., d/2 with outputs (a + b, a - b).
@@ -23,7 +26,7 @@ import numpy as np
 
 __all__ = [
     "E4M3_MAX", "QBLOCK", "sylvester", "fwht_f32", "incoherent_f32", "e4m3_decode", "e4m3_encode",
-    "block_quantize", "tensor_quantize", "dequantize",
+    "block_quantize", "tensor_quantize", "dequantize", "pow2_scale",
 ]
 
 E4M3_MAX = 448.0
@@ -112,8 +115,21 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def block_quantize(x: np.ndarray, block: int = QBLOCK):
-    """x float32 [B,H,N,d] -> (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)])."""
+def pow2_scale(amax: np.ndarray) -> np.ndarray:
+    """Smallest power of two p with 448 p >= amax (1 where amax == 0), float32.
+
+    With amax = m 2^k, m in [1, 2): amax / 448 = (m / 1.75) 2^(k - 8), and m / 1.75 lies in
+    (1/2, 1] when m <= 1.75, in (1, 2) otherwise, so p = 2^(k - 8) or 2^(k - 7)."""
+    a = np.asarray(amax, dtype=np.float64)
+    frac, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = frac 2^ex, frac in [0.5, 1)
+    m, k = 2.0 * frac, ex - 1                              # a = m 2^k, m in [1, 2)
+    e = np.maximum(k - 8 + (m > 1.75).astype(np.int64), -149)   # at least the smallest float32
+    return np.where(a > 0, np.ldexp(1.0, e), 1.0).astype(np.float32)
+
+
+def block_quantize(x: np.ndarray, block: int = QBLOCK, pow2: bool = False):
+    """x float32 [B,H,N,d] -> (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)]);
+    pow2: each scale rounded up to a power of two (pow2_scale)."""
     x = np.asarray(x, dtype=np.float32)
     B, H, N, d = x.shape
     nb = -(-N // block)
@@ -122,7 +138,10 @@ def block_quantize(x: np.ndarray, block: int = QBLOCK):
     for i in range(nb):
         blk = x[:, :, i * block:(i + 1) * block, :]
         amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
-        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        if pow2:
+            sc = pow2_scale(amax)
+        else:
+            sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
         y = (blk / sc[:, :, None, None]).astype(np.float32)     # float32 division, correctly rounded
         codes[:, :, i * block:(i + 1) * block, :] = e4m3_encode(y)
         scales[:, :, i] = sc

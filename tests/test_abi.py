@@ -78,24 +78,39 @@ def test_bwd_rejects_bad_arguments(kw, code):
 
 def test_prep_rejects_bad_arguments():
     lib = eao.load()
-    assert lib.attn_fp8_prep(NULL, P, P, NULL, 1, 1, 128, 128, NULL) == 1
-    assert lib.attn_fp8_prep(P, P, P, ctypes.c_void_p(0x7F0000001001), 1, 1, 128, 128, NULL) == 1
-    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 0, 128, NULL) == 1
-    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 128, 48, NULL) == 2
+    assert lib.attn_fp8_prep(NULL, P, P, NULL, 1, 1, 128, 128, 0, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, ctypes.c_void_p(0x7F0000001001), 1, 1, 128, 128, 0, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 0, 128, 1, NULL) == 1
+    assert lib.attn_fp8_prep(P, P, P, NULL, 1, 1, 128, 48, 0, NULL) == 2
+
+
+def _dkdv_splits(B, Hq, Hkv, N):
+    """Splits of the dK/dV phase as documented in attn.h."""
+    wg = B * Hkv * -(-N // 128)
+    if Hq // Hkv < 2 or wg >= 256:
+        return 1
+    return min(-(-512 // wg), 2 * (Hq // Hkv))
 
 
 def test_workspace_is_linear_in_n():
     ws = eao.bwd_workspace_size
-    sizes = [ws(2, 8, 2, n, 128) for n in (1024, 2048, 4096, 8192)]
+    sizes = [ws(2, 8, 2, n, 128) for n in (1024, 2048, 4096, 8192, 16384)]
     # per query row: D and LSE * log2(e) (one float each, each array rounded up to 256 bytes)
-    # and the transposed rows of Q and dO (d 16-bit values each) -- never an N x N buffer
-    for n, s in zip((1024, 2048, 4096, 8192), sizes):
+    # and the transposed rows of Q and dO (d 16-bit values each) -- never an N x N buffer; with
+    # few K/V heads and keys, the float dK/dV shares of a split dK/dV phase (also linear in N)
+    for n, s in zip((1024, 2048, 4096, 8192, 16384), sizes):
         rows = 2 * 8 * n
-        assert s == 2 * rows * 4 + 2 * rows * 128 * 2 + 2 * 2 * n * 128 * 2   # Hkv = 2
-    # rows are padded to whole tiles of 64
-    assert ws(2, 8, 2, 1000, 128) == sizes[0]
+        split = _dkdv_splits(2, 8, 2, n)
+        part = split * 2 * 2 * 2 * n * 128 * 4 if split > 1 else 0
+        assert s == 2 * rows * 4 + 2 * rows * 128 * 2 + 2 * 2 * n * 128 * 2 + part   # Hkv = 2
+    assert _dkdv_splits(2, 8, 2, 1024) == 8 and _dkdv_splits(2, 8, 2, 16384) == 1
+    # rows are padded to whole tiles of 64 (the shares cover the N rows themselves)
+    assert ws(2, 8, 2, 16383, 128) == sizes[-1]
     assert ws(1, 1, 1, 65, 64) == 2 * 512 + 3 * 128 * 64 * 2
     assert ws(2, 8, 3, 1024, 128) == 0 and ws(1, 1, 1, 1, 80) == 0
+    # variable-length batches never split the phase
+    assert eao.bwd_varlen_workspace_size(2, 8, 2, 1024, 128) == 2 * 2 * 8 * 1024 * 4 + 2 * 2 * 8 * 1024 * 128 * 2 + \
+        2 * 2 * 1024 * 128 * 2
 
 
 def splitkv(**kw):
@@ -109,7 +124,7 @@ def splitkv(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(Nq=0), 1), (dict(Nq=1001), 1), (dict(splits=-1), 1), (dict(scale=0.0), 1),
-    (dict(dtype=2), 2), (dict(d=80), 2), (dict(Hq=8, Hkv=1, Nq=5), 2), (dict(Hq=3, Hkv=2), 1),
+    (dict(dtype=2), 2), (dict(d=80), 2), (dict(Hq=8, Hkv=1, Nq=5), 3), (dict(Hq=3, Hkv=2), 1),
     (dict(), 3), (dict(ws=P, wsb=16), 3),
 ])
 def test_splitkv_rejects_bad_arguments(kw, code):
@@ -122,7 +137,9 @@ def test_splitkv_workspace_size():
     assert ws(1, 8, 2, 1, 100, 128, 1) == 8 * 128 * 4 + 256
     # splits are clamped to the number of 128-key tiles and never empty
     assert ws(1, 8, 2, 1, 300, 128, 64) == ws(1, 8, 2, 1, 300, 128, 3)
-    assert ws(1, 8, 1, 5, 100, 128, 0) == 0     # 8 heads x 5 rows do not fit one 32-row tile
+    # 8 heads x 5 rows per K/V head: two groups of 32 rows, the same partial rows per split
+    assert ws(1, 8, 1, 5, 100, 128, 1) == 8 * 5 * 128 * 4 + 256
+    assert ws(1, 8, 1, 100, 99, 128, 0) == 0    # more query rows than keys
 
 
 def test_fwd_ext_rejects_bad_arguments():
@@ -153,7 +170,8 @@ def test_bwd_varlen_rejects_bad_arguments():
     # q, k, v, o, dout, lse, dq, dk, dv, cu, B, Hq, Hkv, T, max_seqlen, d, causal, scale, dtype, grad dtype,
     # ws, bytes, stream
     need = lib.attn_bwd_varlen_workspace_size(3, 4, 2, 500, 128)
-    assert need == lib.attn_bwd_workspace_size(3, 4, 2, 500, 128) > 0
+    assert 0 < need < lib.attn_bwd_workspace_size(3, 4, 2, 500, 128)    # the dense size adds split shares
+    assert need == lib.attn_bwd_workspace_size(3, 4, 4, 500, 128) - 3 * 2 * 512 * 128 * 2   # Hkv = 4: no split
     a = [P] * 10 + [3, 4, 2, 1000, 500, 128, 1, 0.1, 1, 1, P, need, NULL]
     bad = list(a); bad[9] = NULL                                             # no offsets
     assert lib.attn_bwd_varlen(*bad) == 1
@@ -192,3 +210,13 @@ def test_bwd_ext_rejects_bad_arguments():
     assert lib.attn_bwd_ext(*bad) == 2
     bad = list(a); bad[21] = need - 1                                        # workspace too small
     assert lib.attn_bwd_ext(*bad) == 3
+
+
+def test_clock_probe_rejects_bad_arguments():
+    lib = eao.load()
+    assert lib.attn_clock_probe(NULL, 8, 1000, NULL) == 1
+    assert lib.attn_clock_probe(ctypes.c_void_p(0x7F0000001008), 8, 1000, NULL) == 1   # misaligned
+    assert lib.attn_clock_probe(P, 0, 1000, NULL) == 1
+    assert lib.attn_clock_probe(P, 1025, 1000, NULL) == 1
+    assert lib.attn_clock_probe(P, 8, 0, NULL) == 1
+    assert lib.attn_clock_probe(P, 8, 10 ** 9 + 1, NULL) == 1

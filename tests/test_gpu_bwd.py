@@ -225,3 +225,34 @@ def test_float32_gradients_are_the_accumulators(dtype):
         assert a.dtype == torch.float32 and b.dtype == q.dtype
         assert torch.equal(a.to(b.dtype), b)
         assert _err(a, r) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------- split dK/dV phase (small grouped grids)
+# With few K/V heads and keys (B * Hkv * ceil(N / 128) < 256) the dK/dV phase cuts each key block's
+# (query head, query tile) steps into ranges, keeps each range's share in fp32 and adds the shares
+# in a fixed order.  B=1, Hq=16, Hkv=2, N=2048: 32 key blocks, 16 ranges each.
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_dkdv_small_grouped_grid_full(causal):
+    B, Hq, Hkv, N, d = 1, 16, 2, 2048, 128
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, "bf16", seed=120 + causal)
+    g32 = _gpu_grads(q, k, v, do, causal, grad_dtype=torch.float32)
+    g16 = _gpu_grads(q, k, v, do, causal)
+    refs = A.backward(q, k, v, do, causal, 1.0 / np.sqrt(d))
+    for a, b, r in zip(g32, g16, refs):
+        assert _err(a, r) <= TOL["bf16"]
+        assert torch.equal(a.to(torch.bfloat16), b)
+    # deterministic: the shares are added in a fixed order
+    again = _gpu_grads(q, k, v, do, causal, grad_dtype=torch.float32)
+    for a, b in zip(g32, again):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("Hq,Hkv,N", [(8, 1, 129), (6, 2, 1), (32, 4, 700), (12, 3, 64)])
+def test_split_dkdv_edge_shapes(Hq, Hkv, N):
+    """Ranges that start inside a head's tiles, single-tile heads, ragged tails, one key."""
+    q, k, v, do = _inputs(1, Hq, Hkv, N, 128, "bf16", seed=130 + N)
+    dq, dk, dv = _gpu_grads(q, k, v, do, True, grad_dtype=torch.float32)
+    rq, rk, rv = A.backward(q, k, v, do, True, 1.0 / np.sqrt(128))
+    assert _err(dq, rq) <= TOL["bf16"]
+    assert _err(dk, rk) <= TOL["bf16"]
+    assert _err(dv, rv) <= TOL["bf16"]

@@ -1,9 +1,9 @@
 """GPU parity of the split-KV (decoding) forward against the fp64 oracle, through the C ABI.
 
 Tolerances as for the main forward: O max-abs <= 2e-3 (fp16) / 1.5e-2 (bf16), LSE max-abs
-<= 1e-3.  Small problems are compared over every output; the decoding workloads (8 x 32 heads
-against 32k keys; 4 query rows x 4 x 32 heads against 8k keys) on a sample of heads that the
-oracle computes head by head.
+<= 1e-3.  Small problems are compared over every output, including more than 32 query rows per
+K/V head (several 32-row groups); the decoding workloads (8 x 32 heads against 32k keys; 4 query
+rows x 4 x 32 heads against 8k keys) on a sample of heads that the oracle computes head by head.
 """
 import numpy as np
 import pytest
@@ -44,6 +44,12 @@ CASES = [
     (1, 2, 2, 20, 20, 128, "bf16", True, 2),
     (3, 6, 3, 3, 255, 128, "fp16", False, 2),
     (1, 16, 2, 4, 128, 64, "fp16", True, 0),
+    # more than 32 rows per K/V head: several groups of 32 rows, the last one ragged
+    (1, 32, 4, 8, 1500, 128, "bf16", True, 0),
+    (2, 16, 1, 5, 700, 128, "bf16", True, 3),
+    (1, 8, 8, 33, 1000, 64, "fp16", False, 2),
+    (1, 40, 1, 1, 4096, 128, "bf16", False, 0),
+    (1, 2, 1, 100, 100, 128, "fp16", True, 1),
 ]
 
 
@@ -88,6 +94,19 @@ def test_decode_workloads_sampled_heads(name):
         ro, rlse = DC.forward(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], w.causal, w.scale)
         assert np.abs(o[b, h] - ro[0, 0]).max() <= TOL_O[w.dtype], (b, h)
         assert np.abs(lse[b, h] - rlse[0, 0]).max() <= TOL_LSE, (b, h)
+
+
+def test_row_groups_match_one_group_per_call():
+    # 64 rows per K/V head (two groups of 32): each query head's result is bit for bit that of a
+    # call on the heads of its 32-row group alone (a row's arithmetic does not depend on the
+    # other rows of the launch)
+    q, k, v = _inputs(1, 16, 2, 8, 1111, 128, "bf16", seed=17)
+    o, lse = _run(q, k, v, True, 2)
+    for g in range(2):
+        for part in range(2):
+            hs = slice(8 * g + 4 * part, 8 * g + 4 * part + 4)
+            o1, l1 = _run(q[:, hs], k[:, g:g + 1], v[:, g:g + 1], True, 2)
+            assert np.array_equal(o1, o[:, hs]) and np.array_equal(l1, lse[:, hs]), (g, part)
 
 
 def test_workspace_contents_do_not_matter():

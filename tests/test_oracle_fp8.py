@@ -120,3 +120,43 @@ def test_tensor_quantize_properties():
     bound = np.abs(x) * 2.0 ** -4 + float(scales[0, 0, 0]) * 2.0 ** -10
     assert np.all(np.abs(deq - x) <= bound + 1e-12)
     assert np.all(fp8.tensor_quantize(np.zeros((1, 1, 5, 4), np.float32))[1] == 1.0)
+
+
+def test_pow2_scale_worked_values_and_definition():
+    """The power-of-two block scale is the smallest p = 2^e with 448 p >= amax: worked values, then
+    the definition checked by brute force over a wide range of magnitudes."""
+    worked = {448.0: 1.0, 449.0: 2.0, 224.0: 0.5, 224.00002: 1.0, 447.99997: 1.0, 896.0: 2.0, 3.5: 2.0 ** -7,
+              1.0: 2.0 ** -8, 0.0: 1.0}
+    for a, p in worked.items():
+        assert fp8.pow2_scale(np.float32(a)) == np.float32(p), (a, p)
+    rng = np.random.default_rng(7)
+    a = (np.exp(rng.uniform(-60, 60, size=20000)) * rng.uniform(0.5, 2.0, size=20000)).astype(np.float32)
+    a = np.concatenate([a, (448.0 * np.ldexp(1.0, np.arange(-100, 100))).astype(np.float32)])
+    p = fp8.pow2_scale(a).astype(np.float64)
+    _, ex = np.frexp(p)
+    assert np.all(np.frexp(p)[0] == 0.5)                  # a power of two
+    assert np.all(448.0 * p >= a)                          # large enough
+    assert np.all(448.0 * p / 2 < a)                       # and the smallest such
+
+
+def test_block_quantize_pow2():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((1, 2, 300, 16)).astype(np.float32) * 3
+    x[0, 1, :128] = 0.0
+    codes, scales = fp8.block_quantize(x, pow2=True)
+    c_amax, s_amax = fp8.block_quantize(x)
+    assert scales[0, 1, 0] == 1.0 and np.all(codes[0, 1, :128] == 0)
+    for b, h, i in np.ndindex(1, 2, 3):
+        blk = x[b, h, i * 128:(i + 1) * 128]
+        if not np.any(blk):
+            continue
+        assert scales[b, h, i] == fp8.pow2_scale(np.abs(blk).max())
+        # dividing by a power of two is exact, so the codes are the rounding of x / scale itself
+        assert np.array_equal(codes[b, h, i * 128:(i + 1) * 128],
+                              fp8.e4m3_encode(blk.astype(np.float64) / float(scales[b, h, i])))
+        # the block's largest element lands in the top binade (224, 448]
+        top = np.abs(fp8.e4m3_decode(codes[b, h, i * 128:(i + 1) * 128])).max()
+        assert 224.0 <= top <= 448.0
+    deq = fp8.dequantize(codes, scales)
+    bound = np.abs(x) * 2.0 ** -4 + np.repeat(scales, 128, axis=2)[:, :, :300, None] * 2.0 ** -10
+    assert np.all(np.abs(deq - x) <= bound + 1e-12)
