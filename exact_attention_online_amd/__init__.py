@@ -12,13 +12,13 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "splitkv_workspace_size", "attention", "clock_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
+    "fwd_splitkv", "fwd_splitkv_noalloc", "splitkv_workspace_size", "attention", "clock_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
 ]
 
 F16, BF16, FP8_E4M3, F32 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
-           "attn_clock_probe", "attn_status_string")
+           "attn_fwd_splitkv_noalloc", "attn_clock_probe", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -68,6 +68,8 @@ def load():
     lib.attn_fwd_splitkv_workspace_size.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, sz, vp]
     lib.attn_fwd_splitkv.restype = i
+    lib.attn_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp]
+    lib.attn_fwd_splitkv_noalloc.restype = i
     lib.attn_fp8_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.attn_fp8_prep.restype = i
     lib.attn_clock_probe.argtypes = [vp, i, ctypes.c_longlong, vp]
@@ -249,6 +251,29 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     _check(load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                                    int(bool(causal)), scale, dt, int(num_splits), _ptr(workspace), wsb,
                                    _stream(q.device)))
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q, k, v, out, lse, causal: bool = False, scale: float | None = None, num_splits: int = 0):
+    """fwd_splitkv without a workspace: the split partials go to the library's static scratch buffer
+    on the GPU (ATTN_SPLITKV_SCRATCH_BYTES, 8 MiB), so neither this call nor the library allocates;
+    the caller passes out [B,Hq,Nq,d] and lse [B,Hq,Nq] (float32).  Calls that overlap on one GPU
+    share that buffer and race: serialise them."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise AttnError(f"expected q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise AttnError("q and k/v disagree in B or d")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise AttnError("q, k, v must be contiguous device tensors of one dtype on one device")
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _req(q.device, out=(out, q.shape, q.dtype), lse=(lse, (B, Hq, Nq), torch.float32))
+    _check(load().attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                           int(bool(causal)), scale, dt, int(num_splits), _stream(q.device)))
     return out, lse
 
 

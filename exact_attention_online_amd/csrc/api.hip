@@ -46,6 +46,8 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               void* workspace, hipStream_t stream);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 hipError_t launch_clock_probe(unsigned long long* out, int groups, long long ticks, hipStream_t stream);
+size_t splitkv_scratch_bytes();
+hipError_t splitkv_scratch_address(void** out);
 }  // namespace eao
 
 namespace {
@@ -79,6 +81,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128)";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_SCRATCH: return "problem needs more than the static scratch of the allocation-free entry point (8 MiB)";
     default: return "unknown status";
   }
 }
@@ -293,6 +296,31 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (workspace_bytes < eao::splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)) return ATTN_ERR_WORKSPACE;
   return eao::launch_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal != 0, softmax_scale,
                                  dtype == ATTN_BF16, num_splits, workspace, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                             int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, int dtype,
+                             int num_splits, attn_stream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID;
+  if (!scale_ok(softmax_scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return dtype == ATTN_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID;
+  const int st = check_splitkv(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if (st != ATTN_OK) return st;
+  if (eao::splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits) > eao::splitkv_scratch_bytes())
+    return ATTN_ERR_SCRATCH;
+  // the scratch address is per device: the stream must run on the current device
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return ATTN_ERR_HIP;
+    if ((int)sdev != cur) return ATTN_ERR_INVALID;
+  }
+  void* ws = nullptr;
+  if (eao::splitkv_scratch_address(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  return eao::launch_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal != 0, softmax_scale,
+                                 dtype == ATTN_BF16, num_splits, ws, (hipStream_t)stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -23,11 +23,49 @@
 //
 // Causal alignment for Nq < Nk (bottom-right): query i sits at position Nk - Nq + i and sees
 // keys j <= Nk - Nq + i.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 
 namespace eao {
 
 constexpr int kSkTile = 128;   // keys per tile (32 per wave)
+
+// Static scratch of the allocation-free entry point: the split partials (float O and LSE of
+// every split) live here instead of in a caller's workspace.  Each GPU holds its own copy for
+// the life of the process.  In host code `scratch` only names the symbol; its device address
+// comes from hipGetSymbolAddress (splitkv_scratch_address below) and is the only form passed to
+// kernels.
+constexpr size_t kSplitkvScratchBytes = (size_t)8 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kSplitkvScratchBytes];
+
+size_t splitkv_scratch_bytes() { return kSplitkvScratchBytes; }
+
+// Device address of `scratch` on the current device: looked up once per device (with that
+// device current, as the entry point runs) and kept.
+hipError_t splitkv_scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex init_mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(init_mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 // groups of 32 query rows per K/V head
 static int splitkv_row_groups(int Hq, int Hkv, int Nq) { return ((Hq / Hkv) * Nq + 31) / 32; }

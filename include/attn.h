@@ -57,7 +57,8 @@ typedef enum {
   ATTN_ERR_INVALID = 1,     /* null/misaligned pointer, bad size, bad scale, bad dtype */
   ATTN_ERR_UNSUPPORTED = 2, /* well-formed but not built: head dim other than 64/128, ... */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than attn_bwd_workspace_size() */
-  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+  ATTN_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+  ATTN_ERR_SCRATCH = 5      /* larger than the static scratch of attn_fwd_splitkv_noalloc */
 } attn_status_t;
 
 /* Forward pass.
@@ -218,6 +219,22 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
                      int dtype, int num_splits, void* workspace, size_t workspace_bytes,
                      attn_stream_t stream);
+
+/* attn_fwd_splitkv without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments and results as for attn_fwd_splitkv (same kernels, same split plan, so the same
+ * outputs bit for bit).  The split partials go to a static device buffer of
+ * ATTN_SPLITKV_SCRATCH_BYTES (8 MiB) per GPU that the library holds until the process ends; the
+ * call allocates nothing.  A problem whose attn_fwd_splitkv_workspace_size exceeds the buffer
+ * returns ATTN_ERR_SCRATCH and enqueues nothing.  The stream must belong to the current device
+ * (else ATTN_ERR_INVALID).  Every call on one GPU shares that GPU's buffer, which keeps the last
+ * call's contents (nothing in it needs clearing: each call writes every partial it reads), so
+ * calls that overlap on one GPU -- on different streams or from different threads -- race and
+ * must be serialised by the caller.  Returns an attn_status_t. */
+#define ATTN_SPLITKV_SCRATCH_BYTES ((size_t)8 << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                             float softmax_scale, int dtype, int num_splits, attn_stream_t stream);
 
 /* FP8 preparation ("FlashAttention-3 ...", abstract: block quantisation and incoherent
  * processing).  x float [B,H,N,d]; when signs (int8 [d], entries +1/-1) is not NULL each row is

@@ -32,8 +32,9 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = eao.load()
-    for code in range(5):
+    for code in range(6):
         assert lib.attn_status_string(code)
+    assert b"scratch" in lib.attn_status_string(5)
     assert lib.attn_status_string(99) == b"unknown status"
 
 
@@ -220,3 +221,20 @@ def test_clock_probe_rejects_bad_arguments():
     assert lib.attn_clock_probe(P, 1025, 1000, NULL) == 1
     assert lib.attn_clock_probe(P, 8, 0, NULL) == 1
     assert lib.attn_clock_probe(P, 8, 10 ** 9 + 1, NULL) == 1
+
+
+def test_splitkv_noalloc_rejects_on_the_host():
+    """The allocation-free split-KV entry point checks its arguments, and that the problem's
+    partials fit its static scratch, before any HIP call (so without a GPU too)."""
+    lib = eao.load()
+    ok = [P, P, P, P, P, 1, 8, 2, 1, 1000, 128, 1, 0.1, 1, 0, NULL]
+    bad = list(ok); bad[0] = NULL
+    assert lib.attn_fwd_splitkv_noalloc(*bad) == 1
+    bad = list(ok); bad[8] = 1001                                        # Nq > Nk
+    assert lib.attn_fwd_splitkv_noalloc(*bad) == 1
+    bad = list(ok); bad[13] = 2                                          # fp8
+    assert lib.attn_fwd_splitkv_noalloc(*bad) == 2
+    # 16 x 64 heads x 64 rows, 32k keys: far more partials than 8 MiB
+    big = [P, P, P, P, P, 16, 64, 64, 64, 32768, 128, 1, 0.1, 1, 0, NULL]
+    assert lib.attn_fwd_splitkv_workspace_size(16, 64, 64, 64, 32768, 128, 0) > (8 << 20)
+    assert lib.attn_fwd_splitkv_noalloc(*big) == 5
