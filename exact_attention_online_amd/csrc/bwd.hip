@@ -8,31 +8,30 @@
 //   dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three kernels on the caller's stream, none of them atomic:
-//   1. bwd_pre: per query row -D = -rowsum(dO * O) and LSE * log2(e), and the 64-row tiles of
-//      Q, dO and K written transposed ([d][64 rows], see the workspace layout below), all in the
-//      caller's workspace.
+//   1. bwd_pre: per query row -D = -rowsum(dO * O) and LSE * log2(e), in the caller's workspace.
 //   2. bwd_dkdv: one workgroup of 8 waves per (batch, K/V head, block of 128 keys), in two
 //      roles over the same four quarters of 32 keys (one wave of each role per SIMD).  A "P
 //      wave" keeps its keys' K fragments and dV^T in registers, a "dS wave" their V fragments
 //      and dK^T.  The workgroup walks every query head of the K/V head's group and every tile
 //      of 64 query rows (causal: from the diagonal on), so dK and dV are summed over the group
-//      in registers.  The tiles of Q, dO, Q^T and dO^T and the rows' LSE2 and -D go straight
-//      from HBM into double-buffered LDS (direct buffer -> LDS loads, one tile ahead).  Per
+//      in registers.  The row-major tiles of Q and dO and the rows' LSE2 and -D go straight
+//      from HBM into triple-buffered LDS (direct buffer -> LDS loads, two tiles ahead).  Per
 //      tile (a lane owns one key column of every accumulator):
-//        P wave:  S = Q K^T;  P = exp2(S * scale * log2e - LSE * log2e) (causal mask on the
-//                 diagonal tiles only), rounded to the input type and passed to the partner
-//                 through LDS;  dV^T += dO^T P
+//        P wave:  P = exp2(S * scale * log2e - LSE * log2e) from the S computed one tile earlier
+//                 (causal mask on the diagonal tiles only), rounded to the input type and
+//                 passed to the partner through LDS;  dV^T += dO^T P;  S = Q K^T of the next tile
 //        dS wave: dP - D = dO V^T accumulated from -D;  dS = P (dP - D);  dK^T += Q^T dS
-//      with Q, dO read as rows of the row-major tiles and dO^T, Q^T as rows of the transposed
-//      tiles (all ds_read_b128).  Two contractions per wave keep each wave under 256
-//      registers, so two waves share a SIMD and one's vector work overlaps the other's MFMAs.
+//      Q and dO are read as rows (ds_read_b128), dO^T and Q^T from the same tiles through
+//      ds_read_b64_tr_b16.  Computing S a tile ahead lets the P wave's exponentials run while
+//      the dS wave's dP MFMAs occupy the matrix core.  Two contractions per wave (three MFMA
+//      groups for the P wave) keep each wave under 256 registers, so two waves share a SIMD.
 //   3. bwd_dq: one workgroup of 8 waves per (batch, query head, block of 256 query rows),
 //      shaped like the forward: a lane owns one query row, so LSE and D are one register each.
 //      Per key tile of 64:
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T,
 //      with dS^T fed from the accumulator into the last MFMA (k relabelled as in the forward)
-//      and K^T read as rows of the transposed tiles from bwd_pre; dQ = scale * dQ^T is written
-//      once at the end.
+//      and K^T read from the row-major K tile through ds_read_b64_tr_b16; dQ = scale * dQ^T is
+//      written once at the end.
 // Splitting dQ off costs two extra contractions (S and dP are recomputed) but replaces the
 // fp32 atomic accumulation of dQ, whose ordered completion stalled the loads of the
 // key-stationary kernel, with plain register accumulation.
@@ -55,17 +54,10 @@ constexpr int kBwdRows = 64;    // query rows per dK/dV step (one tile)
 constexpr int kDqRows = 256;    // query rows per dQ workgroup (8 waves x 32; 4 x 32 on small grids)
 constexpr int kDqKeys = 64;     // keys per dQ step
 
-// Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256),
-// T = B * Hq * Npad * d * 2:
+// Workspace layout (bytes), Npad = 64 * ceil(N / 64), A = roundup(B * Hq * Npad * 4, 256):
 //   [0, A)           -D    float  [B*Hq][Npad]   -rowsum(dO * O); 0 past N
 //   [A, 2A)          LSE2  float  [B*Hq][Npad]   LSE * log2(e); +inf past N
-//   [2A, 2A + T)     Q^T   16-bit [B*Hq][Npad/64][d][64]
-//   [2A + T, 2A+2T)  dO^T  16-bit [B*Hq][Npad/64][d][64]
-//   [2A+2T, +Tk)     K^T   16-bit [B*Hkv][Npad/64][d][64], Tk = B * Hkv * Npad * d * 2
-// Within each 64-row tile of Q^T / dO^T / K^T, row d holds the tile's 64 values of column d with the
-// queries of every group of 16 permuted (position 8g + e holds query 8(e/4) + 4g + e%4): a
-// 16-byte read at position 8g then matches the order in which an MFMA accumulator holds the
-// probabilities, so the transposed operands of dV and dK are plain row reads.
+//   [2A, ...)        fp32 dK/dV shares of a split dK/dV phase (dkdv_splits > 1)
 // Row range of sequence b in a packed variable-length batch: cu_seqlens entries clamped to
 // [0, T] and made non-decreasing, and the length capped at the workspace rows per head (npad),
 // so that a malformed array cannot send a kernel outside its buffers.
@@ -81,26 +73,18 @@ __device__ __forceinline__ SeqRange seq_range(const int* __restrict__ cu, int b,
 struct BwdWs {
   float* dsum;
   float* lse2;
-  uint16_t* qt;
-  uint16_t* dot;
-  uint16_t* kt;
   float* part;      // fp32 dK/dV shares of a split dK/dV phase (dkdv_splits > 1)
   int npad;
 };
 
-static BwdWs bwd_ws(void* workspace, int B, int Hq, int Hkv, int N, int d) {
+static BwdWs bwd_ws(void* workspace, int B, int Hq, int N) {
   BwdWs w;
   w.npad = (N + kBwdRows - 1) / kBwdRows * kBwdRows;
   const size_t a = ((size_t)B * Hq * w.npad * 4 + 255) / 256 * 256;
-  const size_t t = (size_t)B * Hq * w.npad * d * 2;
-  const size_t tk = (size_t)B * Hkv * w.npad * d * 2;
   char* base = (char*)workspace;
   w.dsum = (float*)base;
   w.lse2 = (float*)(base + a);
-  w.qt = (uint16_t*)(base + 2 * a);
-  w.dot = (uint16_t*)(base + 2 * a + t);
-  w.kt = (uint16_t*)(base + 2 * a + 2 * t);
-  w.part = (float*)(base + 2 * a + 2 * t + tk);
+  w.part = (float*)(base + 2 * a);
   return w;
 }
 
@@ -120,83 +104,33 @@ int dkdv_splits(int B, int Hq, int Hkv, int N) {
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, bool dense) {
   const size_t npad = (size_t)(N + kBwdRows - 1) / kBwdRows * kBwdRows;
   const size_t a = ((size_t)B * Hq * npad * 4 + 255) / 256 * 256;
-  size_t bytes = 2 * a + 2 * (size_t)B * Hq * npad * d * 2 + (size_t)B * Hkv * npad * d * 2;
+  size_t bytes = 2 * a;
   const int ns = dense ? dkdv_splits(B, Hq, Hkv, N) : 1;
   if (ns > 1) bytes += (size_t)ns * 2 * B * Hkv * N * d * 4;
   return bytes;
 }
 
 // ------------------------------------------------------------------ 1. preprocess
-// Row tile [64][D] in padded LDS (row stride STR) -> transposed tile [D][64] at dst, queries
-// (keys) permuted within each group of 16 as described with the workspace layout.  Eight
-// threads write one 128-byte row of the transposed tile.
-template <int D, int STR>
-__device__ __forceinline__ void write_transposed(const uint16_t* t, uint16_t* __restrict__ dst, int tid) {
-  const int p0 = 8 * (tid & 7);              // first position of this thread's group
-#pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d = (tid >> 3) + 32 * k;
-    uint16_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pp = p0 + e;                 // position within the tile row
-      const int s16 = pp & 15;               // slot 8g + e' within its 16-group
-      const int r = (pp & ~15) + 8 * ((s16 & 7) >> 2) + 4 * (s16 >> 3) + (s16 & 3);
-      v[e] = t[r * STR + d];
-    }
-    *(uint4*)(dst + (size_t)d * kBwdRows + p0) = *(const uint4*)v;
-  }
-}
-
-// Workgroups [0, B*Hq*ntile): one (batch * query head, 64-row tile) each: D and LSE2 of the
-// tile's rows, and the tiles of Q and dO written transposed.  Workgroups after that: one
-// (batch * K/V head, 64-row tile) each, the tile of K written transposed.  Rows past N are
-// zeros.  Loads: 16-byte chunk tid + 256 i of the tile, so each wave reads whole rows.
+// One workgroup of 256 threads per (batch * query head, 64-row tile): -D and LSE2 of the tile's
+// rows.  Thread t reads the 16-byte chunks t + 256 i of the tile's O and dO rows, so the D / 8
+// threads of one row are consecutive lanes and one row sum is a shuffle reduction.  Rows past
+// N get -D = 0 and LSE2 = +inf.
 //
-// VARLEN: sequences packed without padding, Q/O/dO [Hq,T,d], K [Hkv,T,d], LSE [Hq,T] (T = N_in
-// rows), sequence b = rows cu_seqlens[b] .. cu_seqlens[b+1]-1; the workspace keeps the
-// [B*H][npad] layout with npad from the longest sequence, and tiles past a sequence's end are
-// neither read nor written.
+// VARLEN: sequences packed without padding, O/dO [Hq,T,d], LSE [Hq,T] (T = N_in rows),
+// sequence b = rows cu_seqlens[b] .. cu_seqlens[b+1]-1; the workspace keeps the [B*H][npad]
+// layout with npad from the longest sequence, and tiles past a sequence's end are not written.
 template <bool BF16, int D, bool VARLEN = false>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
-                                                      const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                                                      const uint16_t* __restrict__ K, float* __restrict__ Dsum,
-                                                      float* __restrict__ Lse2, uint16_t* __restrict__ QT,
-                                                      uint16_t* __restrict__ dOT, uint16_t* __restrict__ KT, int N_in,
-                                                      int npad, int nq_blocks, int Hq, int Hkv,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE, float* __restrict__ Dsum,
+                                                      float* __restrict__ Lse2, int N_in, int npad, int Hq,
                                                       const int* __restrict__ cu_seqlens) {
-  constexpr int STR = D + 8;                 // padded LDS row (16-bit elements)
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int CPT = kBwdRows * CH / 256;   // chunks per thread per tile
-  __shared__ uint16_t tq[kBwdRows * STR], tdo[kBwdRows * STR];
   const int ntile = npad / kBwdRows;
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x >= nq_blocks) {
-    const int idx = blockIdx.x - nq_blocks;
-    const int bkv = idx / ntile, tile = idx % ntile;
-    int N = N_in;
-    size_t row0 = (size_t)bkv * N_in;
-    if constexpr (VARLEN) {
-      const SeqRange sr = seq_range(cu_seqlens, bkv / Hkv, N_in, npad);
-      if (tile * kBwdRows >= sr.n) return;
-      N = sr.n;
-      row0 = (size_t)(bkv % Hkv) * N_in + sr.s0;
-    }
-    const uint16_t* src = K + (row0 + (size_t)tile * kBwdRows) * D;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
-      uint4 kv = {0, 0, 0, 0};
-      if (tile * kBwdRows + row < N) kv = *(const uint4*)(src + (size_t)row * D + 8 * ch);
-      *(uint4*)(tq + row * STR + 8 * ch) = kv;
-    }
-    __syncthreads();
-    write_transposed<D, STR>(tq, KT + ((size_t)bkv * ntile + tile) * D * kBwdRows, tid);
-    return;
-  }
   const int bh = blockIdx.x / ntile, tile = blockIdx.x % ntile;
   int N = N_in;
-  size_t row0 = (size_t)bh * N_in;             // first row of the head (sequence) in Q, O, dO, LSE
+  size_t row0 = (size_t)bh * N_in;             // first row of the head (sequence) in O, dO, LSE
   if constexpr (VARLEN) {
     const SeqRange sr = seq_range(cu_seqlens, bh / Hq, N_in, npad);
     if (tile * kBwdRows >= sr.n) return;
@@ -204,22 +138,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     row0 = (size_t)(bh % Hq) * N_in + sr.s0;
   }
   const size_t base = (row0 + (size_t)tile * kBwdRows) * D;
+  uint4 ov[CPT], dv[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
+    ov[i] = dv[i] = uint4{0, 0, 0, 0};
+    if (tile * kBwdRows + row < N) {
+      ov[i] = *(const uint4*)(O + base + (size_t)row * D + 8 * ch);
+      dv[i] = *(const uint4*)(dO + base + (size_t)row * D + 8 * ch);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ci = tid + 256 * i, row = ci / CH, ch = ci % CH;
     const int q = tile * kBwdRows + row;
-    uint4 qv = {0, 0, 0, 0}, ov = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
-    if (q < N) {
-      qv = *(const uint4*)(Q + base + (size_t)row * D + 8 * ch);
-      ov = *(const uint4*)(O + base + (size_t)row * D + 8 * ch);
-      dv = *(const uint4*)(dO + base + (size_t)row * D + 8 * ch);
-    }
-    const uint16_t* o16 = (const uint16_t*)&ov;
-    const uint16_t* d16 = (const uint16_t*)&dv;
+    const uint16_t* o16 = (const uint16_t*)&ov[i];
+    const uint16_t* d16 = (const uint16_t*)&dv[i];
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += to_float<BF16>(o16[e]) * to_float<BF16>(d16[e]);
-    // the CH lanes holding one row are consecutive
 #pragma unroll
     for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
     if (ch == 0) {
@@ -227,13 +164,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       Dsum[r] = q < N ? -acc : 0.f;
       Lse2[r] = q < N ? LSE[row0 + q] * kLog2e : INFINITY;
     }
-    *(uint4*)(tq + row * STR + 8 * ch) = qv;
-    *(uint4*)(tdo + row * STR + 8 * ch) = dv;
   }
-  __syncthreads();
-  const size_t dst = ((size_t)bh * ntile + tile) * D * kBwdRows;
-  write_transposed<D, STR>(tq, QT + dst, tid);
-  write_transposed<D, STR>(tdo, dOT + dst, tid);
 }
 
 // One gradient row from an accumulator whose register r of block db holds column
@@ -270,17 +201,21 @@ __device__ __forceinline__ void store_row(void* __restrict__ base, size_t elem, 
 // ------------------------------------------------------------------ 2. dK, dV
 // One workgroup of 8 waves per (batch, K/V head, block of 128 keys).  The waves come in two
 // roles over the same four quarters of 32 keys, one wave of each role per SIMD:
-//   P waves (0-3):  hold K and dV^T of their 32 keys; per query tile S = Q K^T, P = exp2(S c -
-//                   LSE2) (causal mask on the diagonal tiles), P rounded to the input type and
-//                   handed to the partner wave through LDS, then dV^T += dO^T P;
+//   P waves (0-3):  hold K and dV^T of their 32 keys; per query tile P = exp2(S c - LSE2) from
+//                   the S computed during the previous tile (causal mask on the diagonal tiles),
+//                   P rounded to the input type and handed to the partner wave through LDS,
+//                   then dV^T += dO^T P and S = Q K^T of the next tile;
 //   dS waves (4-7): hold V and dK^T; dP - D = dO V^T accumulated from -D, then, with the
 //                   partner's P, dS = P (dP - D) and dK^T += Q^T dS.
-// Each wave does two of the four contractions and needs fewer than 256 registers, so two
-// waves share each SIMD and one wave's vector work runs beside the other's MFMAs.  Per step
-// (one 64-row query tile) the tiles [Q | dO] ([64 rows][D], chunks XOR-swizzled by swz) and
-// [Q^T | dO^T] ([D rows][64], chunk c of row r at c ^ ((r / 2) % 8)), and LSE2 and -D of the
-// 64 rows, go straight from HBM into double-buffered LDS (direct buffer -> LDS loads one step
-// ahead, each buffer a distinct LDS object); every operand read is a 16-byte row read.
+// Each wave needs fewer than 256 registers, so two waves share each SIMD; with S one tile
+// ahead, the P wave's exponentials run while the dS wave's dP MFMAs use the matrix core, and
+// the dS wave's products run beside the P wave's MFMAs.  Per step (one 64-row query tile) the
+// tile [Q | dO] ([64 rows][D] each, chunks XOR-swizzled by swz) and LSE2 and -D of the 64 rows
+// go straight from HBM into triple-buffered LDS (direct buffer -> LDS loads two steps ahead,
+// each buffer a distinct LDS object).  Q and dO are read as 16-byte rows (A operands of S and
+// dP), Q^T and dO^T through transposed reads of the same tiles (A operands of dK^T and dV^T).
+// Two barriers per step: A (P of this tile written, next tile landed) and X (this tile's
+// buffer free for the loads of the tile three steps on).
 // VARLEN: packed sequences as in bwd_pre_kernel (K/V/dK/dV [Hkv,T,d], Q/dO [Hq,T,d]); a key block
 // past its sequence's end exits at once.
 // EXT: the sliding window and ALiBi bias of the forward with the same flag (key j visible to query
@@ -292,33 +227,34 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
-    const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT, void* __restrict__ dK,
-    void* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb, float c /* scale * log2(e) */,
-    float scale, const int* __restrict__ cu_seqlens, int window, const float* __restrict__ slopes, int out32,
-    float* __restrict__ part, int nsplit) {
+    void* __restrict__ dK, void* __restrict__ dV, int Hq, int Hkv, int N_in, int npad, int nkb,
+    float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens, int window,
+    const float* __restrict__ slopes, int out32, float* __restrict__ part, int nsplit) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
   constexpr int NW = 8;                              // waves per workgroup
   constexpr int TILE = kBwdRows * D;                 // 16-bit elements per tile
   constexpr int PIECES = TILE * 2 / 1024;            // 1 KB direct-load pieces per tile
   static_assert(PIECES % NW == 0, "each wave moves the same number of pieces of every tile");
   constexpr int PW = PIECES / NW;
+  // [Q | dO] of one query tile, three buffers
   __shared__ __attribute__((aligned(1024))) short qd0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short qd1[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) short tt0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) short tt1[2 * TILE];
-  // [LSE2 of the 64 rows | zeros][-D of the 64 rows | zeros], 1 KB each
+  __shared__ __attribute__((aligned(1024))) short qd2[2 * TILE];
+  // [LSE2 of the 64 rows | unused][-D of the 64 rows | unused], 1 KB each
   __shared__ __attribute__((aligned(1024))) float st0[512];
   __shared__ __attribute__((aligned(1024))) float st1[512];
+  __shared__ __attribute__((aligned(1024))) float st2[512];
   // P of each key quarter: [quarter][slot 2 * half + t][lane], 16 bytes each
   __shared__ __attribute__((aligned(1024))) uint4 pex[4 * 4 * 64];
   auto QD = [&](auto par) -> short* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return qd0; else return qd1;
-  };
-  auto TT = [&](auto par) -> short* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return tt0; else return tt1;
+    if constexpr (decltype(par)::value == 0) return qd0;
+    else if constexpr (decltype(par)::value == 1) return qd1;
+    else return qd2;
   };
   auto ST = [&](auto par) -> float* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return st0; else return st1;
+    if constexpr (decltype(par)::value == 0) return st0;
+    else if constexpr (decltype(par)::value == 1) return st1;
+    else return st2;
   };
 
   const int tid = threadIdx.x;
@@ -372,7 +308,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
   const int nqb = (N + kBwdRows - 1) / kBwdRows;   // query tiles of the sequence
-  const int nqb_ws = npad / kBwdRows;              // tiles per head in the workspace
   // window (0: none; a window of N or more sees everything, so it is capped at N)
   const int W = (EXT && window > 0) ? min(window, N) : 0;
   // query tiles [qstart, qend) hold every row that sees a key of the block
@@ -391,63 +326,55 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   constexpr int kDiag = kBwdKeys / kBwdRows;
 
   // loop-invariant offsets.  Reads (16-bit units): Q / dO rows 32qs + l32 at chunk 2kk + g;
-  // Q^T / dO^T rows 32db + l32 at chunk 4qs + 2t + g.  Direct loads (bytes): piece NW i + w of
-  // a tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
+  // transposed reads (tr_off) for Q^T and dO^T.  Direct loads (bytes): piece NW i + w of a
+  // tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
   int off_row[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) off_row[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
-  const int tsw = (l32 >> 1) & 7;
-  int off_t[2][2];
+  int off_tr[DB][2];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) off_t[qs][t] = l32 * kBwdRows + (((4 * qs + 2 * t + g) ^ tsw) << 3);
-  uint32_t dma_qd[PW], dma_tt[PW];
+    for (int hh = 0; hh < 2; ++hh) off_tr[db][hh] = tr_off<D>(lane, db, hh);
+  uint32_t dma_qd[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int pch = 64 * (NW * i + w) + lane;
     const int r = pch / CH, cc = pch % CH;
     dma_qd[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
-    const int rt = pch / 8, ct = pch % 8;
-    dma_tt[i] = ((uint32_t)rt * kBwdRows + ((ct ^ ((rt >> 1) & 7)) << 3)) * 2;
   }
 
   // Loader state: the block that the next call of load_next fetches (query head ld_hh of the
-  // group, rows ld_q0 ..), and buffer descriptors over that head's Q, dO, transposed tiles and
-  // statistics, rebuilt only when the head changes.
+  // group, rows ld_q0 ..), and buffer descriptors over that head's Q, dO and statistics, rebuilt
+  // only when the head changes.
   const int it0_tile = per_head > 0 ? it0 % per_head : 0;
-  int ld_hh = per_head > 0 ? min(it0 / per_head, G - 1) : 0;
+  const int it0_hh = per_head > 0 ? min(it0 / per_head, G - 1) : 0;
+  int ld_hh = it0_hh;
   int ld_q0 = (qstart + it0_tile) * kBwdRows, ld_left = per_head - it0_tile;
-  __amdgpu_buffer_rsrc_t qrs, ors, qtrs, otrs, srs;
+  __amdgpu_buffer_rsrc_t qrs, ors, srs;
   auto head_rsrcs = [&]() __attribute__((always_inline)) {
     const size_t bhq = (size_t)b * Hq + kvh * G + ld_hh;
     const size_t qoff = head_row0((int)bhq, kvh * G + ld_hh) * D;
     qrs = make_rsrc(Q + qoff, head_bytes);
     ors = make_rsrc(dO + qoff, head_bytes);
-    qtrs = make_rsrc(QT + bhq * nqb_ws * TILE, (uint32_t)nqb * TILE * 2);
-    otrs = make_rsrc(dOT + bhq * nqb_ws * TILE, (uint32_t)nqb * TILE * 2);
     // LSE2 (wave 0) or -D (wave 1) of the head's rows
     srs = make_rsrc((wu == 0 ? Lse2 : Dneg) + bhq * npad, (uint32_t)npad * 4);
   };
   head_rsrcs();
-  // direct loads of the loader's block into buffer `par` (four tiles, and the 64 rows' LSE2
-  // and -D from waves 0 and 1, whose lanes 16-63 fetch rows that are never read), then advance
-  // the loader; after the last block it stays there, so the last step reloads it into the idle
-  // buffer instead of branching around the loads
+  // direct loads of the loader's block into buffer `par` (two tiles, and the 64 rows' LSE2 and
+  // -D from waves 0 and 1, whose lanes 16-63 fetch rows that are never read), then advance the
+  // loader; after the last block it stays there, so the last steps reload it into idle buffers
+  // instead of branching around the loads
   auto load_next = [&](auto par) __attribute__((always_inline)) {
     short* qd = QD(par);
-    short* tt = TT(par);
-    // a row-major tile of rows q0.. and transposed tile q0 / 64 start at the same byte offset
     const uint32_t off = (uint32_t)ld_q0 * D * 2;
+    if (wu < 2) buffer_load16_lds(srs, (short*)(ST(par) + 256 * wu), 16 * lane + (uint32_t)ld_q0 * 4);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int piece = NW * i + wu;
       buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + off);
       buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + off);
-      buffer_load16_lds(qtrs, tt + 512 * piece, dma_tt[i] + off);
-      buffer_load16_lds(otrs, tt + TILE + 512 * piece, dma_tt[i] + off);
     }
-    if (wu < 2) buffer_load16_lds(srs, (short*)(ST(par) + 256 * wu), 16 * lane + (uint32_t)ld_q0 * 4);
     if (ld_left > 1) {
       --ld_left;
       ld_q0 += kBwdRows;
@@ -458,196 +385,228 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       head_rsrcs();
     }
   };
+  // wait until at most one step's loads (the newest) are in flight: the next tile has landed
+  auto wait_but_one_step = [&]() __attribute__((always_inline)) {
+    if (wu < 2) wait_vmem<2 * PW + 1>();
+    else wait_vmem<2 * PW>();
+  };
 
-  // One query block (rows q0 ..) in buffer `par`; the next one is loaded meanwhile into the
-  // other buffer.
-  // ab2: the ALiBi slope of the block's query head in log2 units, negated (EXT only)
-  // mask_tag: 0 (or false) no mask; 1 (or true) masked (causal diagonal; EXT: window, causal and
-  // bias); 2 (EXT) bias only, for tiles wholly inside the band
-  auto step = [&](int q0, float ab2, auto par, auto mask_tag) __attribute__((always_inline)) {
-    constexpr int MODE = (int)decltype(mask_tag)::value;
-    constexpr bool MASK = MODE == 1;
-    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
-    load_next(Other{});
+  // Compute cursor: query head cu_hh of the group and tile cu_t of the head for the current step.
+  int cu_hh = it0_hh, cu_t = it0_tile;
+  const bool alibi = EXT && slopes != nullptr;
+
+  // S = Q K^T of the tile in buffer `par` (P waves): rows 0-31 and 32-63; a lane owns key
+  // kw + l32, register r holds row 32qs + 8(r/4) + 4g + r%4
+  f32x16_t s[2];
+  auto compute_s = [&](auto par) __attribute__((always_inline)) {
     const short* qd = QD(par);
-    const short* tt = TT(par);
-    const float* st = ST(par);
-    // slots of the P exchange (16-byte units): [quarter][2 * half + t][lane]
-    uint4* px = pex + kq * 256 + lane;
-    if (role == 0) {
-      // ---- S = Q K^T for rows 0-31 and 32-63; a lane owns key kw + l32, register r holds
-      // row 32qs + 8(r/4) + 4g + r%4
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(qd + 32 * qs * D + off_row[kk]));
-          s[qs] = mfma32x32x16<BF16>(a, kvf[kk], s[qs]);
-        }
-      // ---- P = exp2(S c - LSE2), rounded to the input type: B operand of dV^T and the partner's dS
-      const int key = kw + l32;
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
+        const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(qd + 32 * qs * D + off_row[kk]));
+        s[qs] = mfma32x32x16<BF16>(a, kvf[kk], s[qs]);
+      }
+  };
+  // P = exp2(S c - LSE2) in place (P waves); MODE 0 no mask, 1 masked (causal diagonal; EXT:
+  // window, causal and bias), 2 (EXT) bias only, for tiles wholly inside the band
+  auto probs = [&](const float* st, int q0, float ab2, auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = (int)decltype(mode_tag)::value;
+    constexpr bool MASK = MODE == 1;
+    const int key = kw + l32;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 l4 = *(const float4*)(st + 32 * qs + 8 * rr + 4 * g);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    for (int qs = 0; qs < 2; ++qs) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rr + e;
-            float p;
-            if constexpr (EXT && MODE != 0) {
-              const int diff = q0 + 32 * qs + 8 * rr + 4 * g + e - key;   // query - key
-              p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, s[qs][r] * c - lv[e]));
-              if constexpr (MASK) {
-                const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
-                if (!vis) p = 0.f;
-              }
-            } else if constexpr (EXT) {
-              p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
-            } else {
-              p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
-              if constexpr (MASK) {
-                if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
-              }
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 l4 = *(const float4*)(st + 32 * qs + 8 * rr + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float p;
+          if constexpr (EXT && MODE != 0) {
+            const int diff = q0 + 32 * qs + 8 * rr + 4 * g + e - key;   // query - key
+            p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, s[qs][r] * c - lv[e]));
+            if constexpr (MASK) {
+              const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
+              if (!vis) p = 0.f;
             }
-            s[qs][r] = p;
+          } else {
+            p = __builtin_amdgcn_exp2f(s[qs][r] * c - lv[e]);
+            if constexpr (MASK) {
+              if (key > q0 + 32 * qs + 8 * rr + 4 * g + e) p = 0.f;
+            }
           }
+          s[qs][r] = p;
         }
       }
-      i16x8_t pb[2][2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          pb[qs][t] = pack8<BF16>(s[qs], 8 * t);
-          px[64 * (2 * qs + t)] = __builtin_bit_cast(uint4, pb[qs][t]);
-        }
-      lds_barrier();   // P is visible to the dS waves
-      // ---- dV^T += dO^T P (slot (g, e) of half t is row 32qs + 16t + 8(e/4) + 4g + e%4)
-      const short* tdo = tt + TILE;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(tdo + 32 * db * kBwdRows + off_t[qs][t]));
-            acc[db] = mfma32x32x16<BF16>(a, pb[qs][t], acc[db]);
-          }
-    } else {
-      // ---- dP - D = dO V^T accumulated from -D (same layout as S)
-      f32x16_t dp[2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 d4 = *(const float4*)(st + 256 + 32 * qs + 8 * rr + 4 * g);
-          dp[qs][4 * rr + 0] = d4.x;
-          dp[qs][4 * rr + 1] = d4.y;
-          dp[qs][4 * rr + 2] = d4.z;
-          dp[qs][4 * rr + 3] = d4.w;
-        }
-      const short* dos = qd + TILE;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(dos + 32 * qs * D + off_row[kk]));
-          dp[qs] = mfma32x32x16<BF16>(a, kvf[kk], dp[qs]);
-        }
-      lds_barrier();   // the partner's P has been written
-      // ---- dS = P (dP - D), packed as the B operand of dK^T
-      i16x8_t sb[2][2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-          const u32x4_t pw = __builtin_bit_cast(u32x4_t, px[64 * (2 * qs + t)]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * t + 2 * e;
-            dp[qs][r] *= lo_to_float<BF16>(pw[e]);
-            dp[qs][r + 1] *= hi_to_float<BF16>(pw[e]);
-          }
-          sb[qs][t] = pack8<BF16>(dp[qs], 8 * t);
-        }
-      // ---- dK^T += Q^T dS
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(tt + 32 * db * kBwdRows + off_t[qs][t]));
-            acc[db] = mfma32x32x16<BF16>(a, sb[qs][t], acc[db]);
-          }
     }
-    // block it + 1 has landed and every wave is done with this block's buffers
-    wait_all_loads();
-    __syncthreads();
   };
 
-  if (it1 > it0) load_next(Par0{});
-  wait_all_loads();
-  __syncthreads();
-  int it = it0;
-  // unmasked steps [it, end) with the buffer parity of each step (step it0 in buffer 0) fixed at
-  // compile time
-  auto run = [&](int end) __attribute__((always_inline)) {
-    if (((it - it0) & 1) && it < end) {
-      step(0, 0.f, Par1{}, std::false_type{});
-      ++it;
+  // One query tile in buffer `par` (the loads of the tile two steps on go into buffer `par` + 2),
+  // as a P wave and as a dS wave.  The roles run separate loops with the same barriers, so each
+  // keeps only its own values in registers.
+  auto p_step = [&](auto par) __attribute__((always_inline)) {
+    using Next = std::integral_constant<int, (decltype(par)::value + 1) % 3>;
+    using Far = std::integral_constant<int, (decltype(par)::value + 2) % 3>;
+    load_next(Far{});
+    const short* qd = QD(par);
+    const float* st = ST(par);
+    // ---- P of this tile (S computed during the previous step)
+    const int q0 = (qstart + cu_t) * kBwdRows;
+    if constexpr (EXT) {
+      const int dmin = q0 - (k0 + kBwdKeys - 1), dmax = q0 + kBwdRows - 1 - k0;   // query - key
+      const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
+      const float ab2 = alibi ? -slopes[kvh * G + cu_hh] * kLog2e : 0.f;
+      if (!inside) probs(st, q0, ab2, std::integral_constant<int, 1>{});
+      else if (alibi) probs(st, q0, ab2, std::integral_constant<int, 2>{});
+      else probs(st, q0, ab2, std::integral_constant<int, 0>{});
+    } else if constexpr (CAUSAL) {
+      if (cu_t < kDiag) probs(st, q0, 0.f, std::integral_constant<int, 1>{});
+      else probs(st, q0, 0.f, std::integral_constant<int, 0>{});
+    } else {
+      probs(st, q0, 0.f, std::integral_constant<int, 0>{});
     }
-    for (; it + 1 < end; it += 2) {
-      step(0, 0.f, Par0{}, std::false_type{});
-      step(0, 0.f, Par1{}, std::false_type{});
+    // rounded to the input type: B operand of dV^T and the partner's dS; P exchange slots
+    // (16-byte units) [quarter][2 * half + t][lane]
+    uint4* px = pex + kq * 256 + lane;
+    i16x8_t pb[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        pb[qs][t] = pack8<BF16>(s[qs], 8 * t);
+        px[64 * (2 * qs + t)] = __builtin_bit_cast(uint4, pb[qs][t]);
+      }
+    wait_but_one_step();
+    lds_barrier();   // A: P is visible to the dS waves, the next tile to every wave
+    // ---- dV^T += dO^T P (slot (g, e) of half t is row 32qs + 16t + 8(e/4) + 4g + e%4)
+    const short* tdo = qd + TILE;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x8_t a = read_tr8(tdo + (32 * qs + 16 * t) * D, off_tr[db]);
+          acc[db] = mfma32x32x16<BF16>(a, pb[qs][t], acc[db]);
+        }
+    // ---- S of the next tile (past the workgroup's last step it reads a reloaded block and the
+    // result is never used)
+    compute_s(Next{});
+    // scheduling: LDS reads a few ahead of their MFMAs (0x100 = LDS reads, 0x008 = MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    if (it < end) {
-      step(0, 0.f, Par0{}, std::false_type{});
-      ++it;
+#pragma unroll
+    for (int i = 0; i < 2 * KK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    lds_barrier();   // X: every wave is done with this tile's buffers (and the P exchange)
+    if (cu_t + 1 < per_head) {
+      ++cu_t;
+    } else {
+      ++cu_hh;
+      cu_t = 0;
     }
   };
-  if constexpr (EXT) {
-    // tiles that cross a window edge or the causal diagonal take the masked path; tiles wholly
-    // inside the band take the bias-only path with ALiBi, the plain path without
-    using Mode0 = std::integral_constant<int, 0>;
-    using Mode1 = std::integral_constant<int, 1>;
-    using Mode2 = std::integral_constant<int, 2>;
-    const bool alibi = slopes != nullptr;
-    for (int hh = 0; hh < G; ++hh) {
-      const int base = hh * per_head;
-      const float ab2 = alibi ? -slopes[kvh * G + hh] * kLog2e : 0.f;
-      for (; it < base + per_head; ++it) {
-        const int q0 = (qstart + it - base) * kBwdRows;
-        const int dmin = q0 - (k0 + kBwdKeys - 1), dmax = q0 + kBwdRows - 1 - k0;   // query - key
-        const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
-        if (it & 1) {
-          if (!inside) step(q0, ab2, Par1{}, Mode1{});
-          else if (alibi) step(q0, ab2, Par1{}, Mode2{});
-          else step(q0, ab2, Par1{}, Mode0{});
-        } else {
-          if (!inside) step(q0, ab2, Par0{}, Mode1{});
-          else if (alibi) step(q0, ab2, Par0{}, Mode2{});
-          else step(q0, ab2, Par0{}, Mode0{});
+  auto ds_step = [&](auto par) __attribute__((always_inline)) {
+    using Far = std::integral_constant<int, (decltype(par)::value + 2) % 3>;
+    load_next(Far{});
+    const short* qd = QD(par);
+    const float* st = ST(par);
+    // ---- dP - D = dO V^T accumulated from -D (same layout as S)
+    f32x16_t dp[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 d4 = *(const float4*)(st + 256 + 32 * qs + 8 * rr + 4 * g);
+        dp[qs][4 * rr + 0] = d4.x;
+        dp[qs][4 * rr + 1] = d4.y;
+        dp[qs][4 * rr + 2] = d4.z;
+        dp[qs][4 * rr + 3] = d4.w;
+      }
+    const short* dos = qd + TILE;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(dos + 32 * qs * D + off_row[kk]));
+        dp[qs] = mfma32x32x16<BF16>(a, kvf[kk], dp[qs]);
+      }
+    wait_but_one_step();
+    lds_barrier();   // A: the partner's P has been written
+    // ---- dS = P (dP - D), packed as the B operand of dK^T
+    const uint4* px = pex + kq * 256 + lane;
+    i16x8_t sb[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+        const u32x4_t pw = __builtin_bit_cast(u32x4_t, px[64 * (2 * qs + t)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          dp[qs][r] *= lo_to_float<BF16>(pw[e]);
+          dp[qs][r + 1] *= hi_to_float<BF16>(pw[e]);
         }
+        sb[qs][t] = pack8<BF16>(dp[qs], 8 * t);
       }
+    // ---- dK^T += Q^T dS
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x8_t a = read_tr8(qd + (32 * qs + 16 * t) * D, off_tr[db]);
+          acc[db] = mfma32x32x16<BF16>(a, sb[qs][t], acc[db]);
+        }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-  } else if constexpr (CAUSAL) {
-    for (int hh = per_head > 0 ? it0 / per_head : G; it < it1; ++hh) {
-      const int base = hh * per_head;
-      const int diag_end = min(min(base + kDiag, base + per_head), it1);
-      for (; it < diag_end; ++it) {
-        const int q0 = (qstart + it - base) * kBwdRows;
-        if ((it - it0) & 1) step(q0, 0.f, Par1{}, std::true_type{});
-        else step(q0, 0.f, Par0{}, std::true_type{});
-      }
-      run(min(base + per_head, it1));
+    lds_barrier();   // X
+  };
+  // steps [it0, it1), step it0 in buffer 0
+  auto run = [&](auto stepf) __attribute__((always_inline)) {
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    int it = it0;
+    for (; it + 3 <= it1; it += 3) {
+      stepf(B0{});
+      stepf(B1{});
+      stepf(B2{});
     }
-  } else {
-    run(it1);
+    if (it < it1) {
+      stepf(B0{});
+      ++it;
+    }
+    if (it < it1) stepf(B1{});
+  };
+
+  if (it1 > it0) {
+    load_next(std::integral_constant<int, 0>{});
+    load_next(std::integral_constant<int, 1>{});
+    wait_but_one_step();
+    lds_barrier();
+    if (role == 0) {
+      compute_s(std::integral_constant<int, 0>{});
+      run(p_step);
+    } else {
+      run(ds_step);
+    }
   }
 
   // epilogue: lane owns key kw + l32; register r holds d = 32db + 8(r/4) + 4g + r%4
@@ -695,10 +654,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restri
 // One workgroup of 8 waves per (batch, query head, block of 256 query rows); a wave owns 32
 // rows (two waves per SIMD).  When 256-row blocks would give the CUs fewer than two workgroups
 // each (dense layout, no window or bias), 4 waves and 128 rows, twice the workgroups; a row's
-// arithmetic is the same either way.  Per key tile of 64, three tiles in double-buffered LDS,
-// each pair of buffers distinct LDS objects, filled by direct buffer -> LDS loads: [K | V] ([64][D],
-// chunks swizzled by swz) and K^T ([D][64] from the preprocess, chunk c of row r at
-// c ^ ((r / 2) % 8)).  All LDS reads are 16-byte rows.
+// arithmetic is the same either way.  Per key tile of 64, the tiles [K | V] ([64][D], chunks
+// swizzled by swz) in double-buffered LDS (two distinct LDS objects), filled by direct
+// buffer -> LDS loads.  K and V are read as 16-byte rows (A operands of S^T and dP^T), K^T
+// through ds_read_b64_tr_b16 of the same K tile (A operand of dQ^T).
 // VARLEN: packed sequences as in bwd_pre_kernel; a query block past its sequence's end exits at
 // once.  EXT: window and ALiBi as in the dK/dV kernel; key tiles outside the block's band are
 // skipped and every other tile takes the masked path with the bias.
@@ -706,7 +665,7 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, 
 __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
-    const uint16_t* __restrict__ KT, void* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
+    void* __restrict__ dQ, int Hq, int Hkv, int N_in, int npad, int BH, int nqb,
     float c /* scale * log2(e) */, float scale, const int* __restrict__ cu_seqlens, int window,
     const float* __restrict__ slopes, int out32) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
@@ -717,13 +676,8 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   constexpr int PW = PIECES / NW;                   // pieces per wave per tile
   __shared__ __attribute__((aligned(1024))) short kv0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short kv1[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) short kt0[TILE];
-  __shared__ __attribute__((aligned(1024))) short kt1[TILE];
   auto KV = [&](auto par) -> short* __attribute__((always_inline)) {
     if constexpr (decltype(par)::value == 0) return kv0; else return kv1;
-  };
-  auto KTs = [&](auto par) -> short* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return kt0; else return kt1;
   };
 
   const int tid = threadIdx.x;
@@ -754,8 +708,6 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + q_row0 * D, head_bytes);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
-  const int ntile_all = npad / kDqKeys;
-  const __amdgpu_buffer_rsrc_t trs = make_rsrc(KT + (size_t)bkv * ntile_all * TILE, (uint32_t)ntile_all * TILE * 2);
 
   const int q0 = qblk * ROWS;
   const int qw = q0 + 32 * w;
@@ -778,36 +730,31 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
   // loop-invariant offsets.  Reads (16-bit units): K / V rows 32kb + l32 at chunk 2kk + g;
-  // K^T rows 32db + l32 at chunk 4kb + 2t + g.  Direct loads (bytes): piece NW i + w of a
-  // tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
+  // K^T through transposed reads of the K tile (tr_off).  Direct loads (bytes): piece NW i + w
+  // of a tile, lane l -> LDS chunk 64(NW i + w) + l, fetched from the chunk the swizzle puts there.
   int off_row[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) off_row[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
-  const int tsw = (l32 >> 1) & 7;
-  int off_t[2][2];
+  int off_tr[DB][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) off_t[kb][t] = l32 * kDqKeys + (((4 * kb + 2 * t + g) ^ tsw) << 3);
-  uint32_t dma_kv[PW], dma_t[PW];
+    for (int hh = 0; hh < 2; ++hh) off_tr[db][hh] = tr_off<D>(lane, db, hh);
+  uint32_t dma_kv[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int pch = 64 * (NW * i + w) + lane;
     const int r = pch / CH, cc = pch % CH;
     dma_kv[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
-    const int rt = pch / 8, ct = pch % 8;
-    dma_t[i] = ((uint32_t)rt * kDqKeys + ((ct ^ ((rt >> 1) & 7)) << 3)) * 2;
   }
   auto load_tiles = [&](int j, auto par) __attribute__((always_inline)) {
     short* kv = KV(par);
-    short* kt = KTs(par);
     const uint32_t rowoff = (uint32_t)j * kDqKeys * D * 2;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int piece = NW * i + w;
       buffer_load16_lds(krs, kv + 512 * piece, dma_kv[i] + rowoff);
       buffer_load16_lds(vrs, kv + TILE + 512 * piece, dma_kv[i] + rowoff);
-      buffer_load16_lds(trs, kt + 512 * piece, dma_t[i] + rowoff);
     }
   };
 
@@ -871,12 +818,11 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   };
   // dQ^T += K^T dS^T (slot (g, e) of half t is key 32kb + 16t + 8(e/4) + 4g + e%4)
   auto dq_mma = [&](auto par, int kb, const i16x8_t (&sb)[2]) __attribute__((always_inline)) {
-    const short* kt = KTs(par);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(kt + 32 * db * kDqKeys + off_t[kb][t]));
+        const i16x8_t a = read_tr8(KV(par) + (32 * kb + 16 * t) * D, off_tr[db]);
         acc[db] = mfma32x32x16<BF16>(a, sb[t], acc[db]);
       }
   };
@@ -896,7 +842,7 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     dq_mma(par, 0, sb0);
     dq_mma(par, 1, sb1);
     // scheduling: LDS reads four ahead of their MFMAs (0x100 = LDS reads, 0x008 = MFMA,
-    // 0x402 = vector ALU)
+    // 0x402 = vector ALU); the dQ MFMAs take two transposed reads each
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -912,13 +858,13 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     wait_all_loads();
     __syncthreads();
@@ -992,13 +938,13 @@ template <bool BF16, int D, bool VARLEN>
 static hipError_t launch_pre_t(const void* q, const void* k, const void* o, const void* dout, const float* lse, int B,
                                int Hq, int Hkv, int N, int max_seqlen, const int* cu, void* workspace,
                                hipStream_t stream) {
-  const BwdWs w = bwd_ws(workspace, B, Hq, Hkv, VARLEN ? max_seqlen : N, D);
-  const int ntile = w.npad / kBwdRows;
-  const int nq_blocks = B * Hq * ntile;
-  const unsigned grid = (unsigned)(nq_blocks + B * Hkv * ntile);
-  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D, VARLEN>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)q,
-                     (const uint16_t*)o, (const uint16_t*)dout, lse, (const uint16_t*)k, w.dsum, w.lse2, w.qt, w.dot,
-                     w.kt, N, w.npad, nq_blocks, Hq, Hkv, cu);
+  (void)q;
+  (void)k;
+  (void)Hkv;
+  const BwdWs w = bwd_ws(workspace, B, Hq, VARLEN ? max_seqlen : N);
+  const unsigned grid = (unsigned)(B * Hq * (w.npad / kBwdRows));
+  hipLaunchKernelGGL((bwd_pre_kernel<BF16, D, VARLEN>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)o,
+                     (const uint16_t*)dout, lse, w.dsum, w.lse2, N, w.npad, Hq, cu);
   return hipGetLastError();
 }
 
@@ -1009,12 +955,12 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
                                 const float* slopes = nullptr) {
   (void)lse;   // the probabilities use LSE * log2(e) from the workspace
   const int rows = VARLEN ? max_seqlen : N;
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, Hkv, rows, D);
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows);
   const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
   const int ns = (VARLEN || EXT) ? 1 : dkdv_splits(B, Hq, Hkv, N);
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv * ns), dim3(512), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                     w.dsum, w.lse2, w.qt, w.dot, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
+                     w.dsum, w.lse2, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
                      slopes, (int)out32, ns > 1 ? w.part : (float*)nullptr, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
@@ -1032,7 +978,7 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
                               const float* slopes = nullptr) {
   (void)lse;
   const int rows = VARLEN ? max_seqlen : N;
-  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, Hkv, rows, D);
+  const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows);
   const int BH = B * Hq;
   // 128-row blocks (4 waves) when 256-row blocks would give the CUs fewer than two workgroups
   // each (plain dense layout only); a row's arithmetic is the same either way
@@ -1042,7 +988,7 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
       const int nqb = (rows + R - 1) / R;
       hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT, R>), dim3(nqb * BH), dim3(R / 32 * 64), 0,
                          stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                         w.dsum, w.lse2, w.kt, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
+                         w.dsum, w.lse2, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
                          slopes, (int)out32);
       return hipGetLastError();
     }
@@ -1050,7 +996,7 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
   const int nqb = (rows + kDqRows - 1) / kDqRows;
   hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                     w.dsum, w.lse2, w.kt, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
+                     w.dsum, w.lse2, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
                      slopes, (int)out32);
   return hipGetLastError();
 }

@@ -169,6 +169,14 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, shor
 // every iteration.
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most n of this wave's vector-memory operations are outstanding (they complete
+// in order, so every older one has finished), without waiting for LDS or scalar loads.
+template <int n>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);   // vmcnt n, expcnt 7, lgkmcnt 15: no other wait
+}
+
 // Workgroup barrier after this wave's LDS accesses have completed (s_waitcnt lgkmcnt(0);
 // s_barrier): makes LDS writes visible to the other waves without waiting for the direct
 // loads in flight, which a full __syncthreads() fence would also wait for.
@@ -179,6 +187,23 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ i16x4_t ds_read_tr16(const short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+// Transposed A operand from a row-major LDS tile (rows x D, swizzled by swz).  For the 16 rows
+// R0 .. R0 + 15 at `base` (R0 a multiple of 16) and columns 32db .. 32db + 31, lane l receives
+// A[row = l % 32][k = 8g + e] = tile[R0 + 8(e/4) + 4g + e%4][32db + l % 32]: the rows in the
+// order in which a C tile's register r = 8t + e holds them, so the B operand can be a C tile of
+// another MFMA packed to 16 bits.  off[hh] = tr_off(lane, db, hh): lane l of each group of 16
+// points at row 4(G16/2) + (l%16)/4 + 8hh, columns 32db + 16(G16%2) + 4(l%4) .. + 3.
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int db, int hh) {
+  const int G16 = lane >> 4, li = lane & 15;
+  return elem_index<D>(4 * (G16 >> 1) + (li >> 2) + 8 * hh, 32 * db + 16 * (G16 & 1) + 4 * (li & 3));
+}
+__device__ __forceinline__ i16x8_t read_tr8(const short* base, const int (&off)[2]) {
+  const i16x4_t lo = ds_read_tr16(base + off[0]);
+  const i16x4_t hi = ds_read_tr16(base + off[1]);
+  return i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 }  // namespace eao

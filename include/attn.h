@@ -145,10 +145,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
                     attn_stream_t stream);
 
 /* Bytes of device workspace attn_bwd needs, linear in N (no N x N buffer); with Npad = N rounded
- * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each, and
- * transposed copies of Q, dO and K in 64-row tiles, 16-bit [B,Hq,Npad,d] (Q, dO) and
- * [B,Hkv,Npad,d] (K), i.e. 2 * roundup(4 * B * Hq * Npad, 256) + 2 * (2 * Hq + Hkv) * B * Npad * d
- * bytes.  Grouped-query problems (Hq > Hkv) whose B * Hkv * ceil(N / 128) is below 256 split the
+ * up to a multiple of 64: -D = -rowsum(dO * O) and LSE * log2(e) as float [B,Hq,Npad] each,
+ * i.e. 2 * roundup(4 * B * Hq * Npad, 256) bytes.  Grouped-query problems (Hq > Hkv) whose B * Hkv * ceil(N / 128) is below 256 split the
  * dK/dV phase S = min(ceil(512 / (B * Hkv * ceil(N / 128))), 2 * Hq / Hkv) ways, so that it fills
  * the GPU, and add S * 2 * B * Hkv * N * d * 4 bytes for the float shares (added in a fixed
  * order, so the gradients stay deterministic).  0 if the sizes are invalid. */
@@ -178,8 +176,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * same arguments and workspace, preprocess followed by dkdv and dq (in either order, or on two
  * streams once preprocess is complete) produces exactly what attn_bwd produces; attn_bwd is
  * these three calls on one stream.
- *   attn_bwd_preprocess: -D = -rowsum(dO * O), LSE * log2(e) and the transposed tiles of q,
- *                        dout and k into the workspace.
+ *   attn_bwd_preprocess: -D = -rowsum(dO * O) and LSE * log2(e) into the workspace (q and k
+ *                        are checked like the other pointers but not read).
  *   attn_bwd_dkdv:       dK, dV written (the probabilities are recomputed from q, k and lse).
  *   attn_bwd_dq:         dQ written (the probabilities are recomputed from q, k and lse).
  * Arguments mean what they mean for attn_bwd (preprocess takes no grad_dtype: it writes only

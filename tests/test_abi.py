@@ -96,22 +96,22 @@ def _dkdv_splits(B, Hq, Hkv, N):
 def test_workspace_is_linear_in_n():
     ws = eao.bwd_workspace_size
     sizes = [ws(2, 8, 2, n, 128) for n in (1024, 2048, 4096, 8192, 16384)]
-    # per query row: D and LSE * log2(e) (one float each, each array rounded up to 256 bytes)
-    # and the transposed rows of Q and dO (d 16-bit values each) -- never an N x N buffer; with
-    # few K/V heads and keys, the float dK/dV shares of a split dK/dV phase (also linear in N)
+    # per query row: -D and LSE * log2(e) (one float each)
+    # -- never an N x N buffer; with few K/V heads and keys, the float dK/dV shares of a split
+    # dK/dV phase (also linear in N)
     for n, s in zip((1024, 2048, 4096, 8192, 16384), sizes):
         rows = 2 * 8 * n
         split = _dkdv_splits(2, 8, 2, n)
         part = split * 2 * 2 * 2 * n * 128 * 4 if split > 1 else 0
-        assert s == 2 * rows * 4 + 2 * rows * 128 * 2 + 2 * 2 * n * 128 * 2 + part   # Hkv = 2
+        assert s == 2 * rows * 4 + part   # Hkv = 2
     assert _dkdv_splits(2, 8, 2, 1024) == 8 and _dkdv_splits(2, 8, 2, 16384) == 1
     # rows are padded to whole tiles of 64 (the shares cover the N rows themselves)
     assert ws(2, 8, 2, 16383, 128) == sizes[-1]
-    assert ws(1, 1, 1, 65, 64) == 2 * 512 + 3 * 128 * 64 * 2
+    assert ws(1, 1, 1, 65, 64) == 2 * 512
+    assert ws(3, 1, 1, 1, 64) == 2 * 3 * 64 * 4
     assert ws(2, 8, 3, 1024, 128) == 0 and ws(1, 1, 1, 1, 80) == 0
     # variable-length batches never split the phase
-    assert eao.bwd_varlen_workspace_size(2, 8, 2, 1024, 128) == 2 * 2 * 8 * 1024 * 4 + 2 * 2 * 8 * 1024 * 128 * 2 + \
-        2 * 2 * 1024 * 128 * 2
+    assert eao.bwd_varlen_workspace_size(2, 8, 2, 1024, 128) == 2 * 2 * 8 * 1024 * 4
 
 
 def splitkv(**kw):
@@ -172,7 +172,7 @@ def test_bwd_varlen_rejects_bad_arguments():
     # ws, bytes, stream
     need = lib.attn_bwd_varlen_workspace_size(3, 4, 2, 500, 128)
     assert 0 < need < lib.attn_bwd_workspace_size(3, 4, 2, 500, 128)    # the dense size adds split shares
-    assert need == lib.attn_bwd_workspace_size(3, 4, 4, 500, 128) - 3 * 2 * 512 * 128 * 2   # Hkv = 4: no split
+    assert need == lib.attn_bwd_workspace_size(3, 4, 4, 500, 128)    # Hkv = 4: no split
     a = [P] * 10 + [3, 4, 2, 1000, 500, 128, 1, 0.1, 1, 1, P, need, NULL]
     bad = list(a); bad[9] = NULL                                             # no offsets
     assert lib.attn_bwd_varlen(*bad) == 1
