@@ -71,7 +71,8 @@ struct FwdTile {
 // [H, T, d] and LSE [H, T] with T = N_in packed tokens; sequence b is rows cu_seqlens[b] ..
 // cu_seqlens[b + 1] - 1 of every head (clamped to [0, T]) and attends only within itself.  The
 // grid covers the longest sequence (nqb blocks of BR rows); blocks past a sequence's end exit.
-template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false, bool VARLEN = false, int NWV = 4>
+template <bool BF16, int D, int QB, int BC, bool CAUSAL, bool EXT = false, bool VARLEN = false, int NWV = 4,
+          bool ALIBI = false>
 __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N_in, int BH, int nqb,
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   // first tile with a key inside the window of the workgroup's first row
   const int jfirst = win ? max(0, q0 - window + 1) / BC : 0;
   // ALiBi in units of the raw scores (the softmax scale multiplies later): -slope / scale
-  const float ab = (EXT && slopes != nullptr) ? -slopes[h] * inv_scale : 0.f;
+  const float ab = ALIBI ? -slopes[h] * inv_scale : 0.f;
 
   // K/V of this head through bounds-checked buffer loads: keys >= N read as zeros
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, (uint32_t)N * D * 2);
@@ -236,8 +237,8 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   // scheduler overlaps matrix and vector work.  MASK selects the variant with causal / key-tail
   // masking.
   f32x16_t sA[QB][KB], sB[QB][KB];   // S^T of even / odd tiles
-  // MODE 0: no mask; 1: masked (causal diagonal, key tail, window edges; ALiBi under EXT);
-  // 2: no mask, ALiBi bias only (EXT tiles inside the band)
+  // MODE 0: no mask; 1: masked (causal diagonal, key tail, window edges; with ALIBI also the
+  // bias); 2: no mask, ALiBi bias only (ALIBI tiles inside the band)
   auto body = [&](int j, auto par, auto mode_tag) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = MODE == 1;
@@ -262,13 +263,13 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float diff = dq - (float)(32 * kb + 8 * (r >> 2) + (r & 3));
-            const float biased = __builtin_fmaf(__builtin_fabsf(diff), ab, sc[qb][kb][r]);
+            float val = sc[qb][kb][r];
+            if constexpr (ALIBI) val = __builtin_fmaf(__builtin_fabsf(diff), ab, val);
             if constexpr (MASK) {
               const bool vis = diff > lo && diff < wf && (CAUSAL ? diff >= 0.f : diff > -wf);
-              sc[qb][kb][r] = vis ? biased : -INFINITY;
-            } else {
-              sc[qb][kb][r] = biased;
+              val = vis ? val : -INFINITY;
             }
+            sc[qb][kb][r] = val;
           }
       } else if constexpr (MASK) {
         const int qrow = qw + 32 * qb + l32;
@@ -385,20 +386,26 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
     }
   };
   if constexpr (EXT) {
-    // one loop (a single register assignment for the running state), the tile's kind and buffer
-    // parity chosen per iteration
-    const bool alibi = ab != 0.f;
-    for (; j < jact; ++j) {
-      const bool inner = j >= jlo && j < jmask;
-      if (j & 1) {
-        if (!inner) body(j, Par1{}, Mode1{});
-        else if (alibi) body(j, Par1{}, Mode2{});
-        else body(j, Par1{}, Mode0{});
-      } else {
-        if (!inner) body(j, Par0{}, Mode1{});
-        else if (alibi) body(j, Par0{}, Mode2{});
-        else body(j, Par0{}, Mode0{});
-      }
+    // the tile's kind chosen per tile, two kinds per instantiation (masked, and bias-only with
+    // ALIBI or plain without); the loop runs over pairs of tiles so that the buffer parity (and
+    // with it which S^T registers hold the current and the next tile) is fixed at compile time
+    // in each half
+    using Inner = std::integral_constant<int, ALIBI ? 2 : 0>;
+    auto ext_body = [&](int jj, auto par) __attribute__((always_inline)) {
+      if (jj >= jlo && jj < jmask) body(jj, par, Inner{});
+      else body(jj, par, Mode1{});
+    };
+    if ((j & 1) && j < jact) {
+      ext_body(j, Par1{});
+      ++j;
+    }
+    for (; j + 2 <= jact; j += 2) {
+      ext_body(j, Par0{});
+      ext_body(j + 1, Par1{});
+    }
+    if (j < jact) {
+      ext_body(j, Par0{});
+      ++j;
     }
   } else {
     // jfirst = jlo = 0: tiles [0, jmask) in pairs of parities 0, 1
@@ -460,16 +467,31 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
   return launch_fwd_nwv<BF16, D, QB, BC, CAUSAL, 8>(q, k, v, o, lse, B, Hq, Hkv, N, scale, stream);
 }
 
+template <bool BF16, int D, bool CAUSAL, int NWV, bool ALIBI>
+static hipError_t launch_fwd_ext_w(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                   int Hkv, int N, float scale, int window, const float* slopes, hipStream_t stream) {
+  constexpr int BR = NWV * 32;
+  const int nqb = (N + BR - 1) / BR;
+  const int BH = B * Hq;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, 1, 64, CAUSAL, true, false, NWV, ALIBI>), dim3(nqb * BH),
+                     dim3(NWV * 64), 0, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     (uint16_t*)o, lse, Hq, Hkv, N, BH, nqb, scale * kLog2e, window, slopes, 1.f / scale,
+                     (const int*)nullptr);
+  return hipGetLastError();
+}
+
+// window / ALiBi: ALiBi is a compile-time switch (each kernel then has two tile kinds); 256-row
+// blocks when they give every CU at least two workgroups, else 128-row blocks
 template <bool BF16, int D, bool CAUSAL>
 static hipError_t launch_fwd_ext_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                    int Hkv, int N, float scale, int window, const float* slopes, hipStream_t stream) {
-  constexpr int BR = 128;
-  const int nqb = (N + BR - 1) / BR;
-  const int BH = B * Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, 1, 64, CAUSAL, true>), dim3(nqb * BH), dim3(256), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N, BH,
-                     nqb, scale * kLog2e, window, slopes, 1.f / scale, (const int*)nullptr);
-  return hipGetLastError();
+  const bool big = (long long)B * Hq * ((N + 255) / 256) >= 2 * kNumCUs;
+  if (slopes != nullptr) {
+    if (big) return launch_fwd_ext_w<BF16, D, CAUSAL, 8, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, window, slopes, stream);
+    return launch_fwd_ext_w<BF16, D, CAUSAL, 4, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, window, slopes, stream);
+  }
+  if (big) return launch_fwd_ext_w<BF16, D, CAUSAL, 8, false>(q, k, v, o, lse, B, Hq, Hkv, N, scale, window, slopes, stream);
+  return launch_fwd_ext_w<BF16, D, CAUSAL, 4, false>(q, k, v, o, lse, B, Hq, Hkv, N, scale, window, slopes, stream);
 }
 
 hipError_t launch_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
