@@ -223,7 +223,7 @@ __device__ __forceinline__ void store_row(void* __restrict__ base, size_t elem, 
 // query head h gets -slopes[h] |i - j| after the softmax scale).  The bias is constant in Q and
 // K, so the gradients keep their form and only the recomputed P changes: every query tile in
 // the band of the key block takes the masked path with the bias, tiles outside it are skipped.
-template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, bool ALIBI = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dneg, const float* __restrict__ Lse2,
@@ -336,12 +336,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) off_tr[db][hh] = tr_off<D>(lane, db, hh);
-  uint32_t dma_qd[PW];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int pch = 64 * (NW * i + w) + lane;
+  // (piece NW i + w lies 64 NW i / CH rows after piece w, a multiple of the swizzle's period, so
+  // its source is dma_qd plus a uniform offset)
+  static_assert((64 * NW / CH) % 16 == 0, "pieces of one wave keep the row swizzle");
+  uint32_t dma_qd;
+  {
+    const int pch = 64 * w + lane;
     const int r = pch / CH, cc = pch % CH;
-    dma_qd[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
+    dma_qd = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
   }
 
   // Loader state: the block that the next call of load_next fetches (query head ld_hh of the
@@ -372,8 +374,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int piece = NW * i + wu;
-      buffer_load16_lds(qrs, qd + 512 * piece, dma_qd[i] + off);
-      buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd[i] + off);
+      const uint32_t soff = off + (uint32_t)i * (64 * NW / CH) * D * 2;
+      buffer_load16_lds(qrs, qd + 512 * piece, dma_qd, soff);
+      buffer_load16_lds(ors, qd + TILE + 512 * piece, dma_qd, soff);
     }
     if (ld_left > 1) {
       --ld_left;
@@ -393,7 +396,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   // Compute cursor: query head cu_hh of the group and tile cu_t of the head for the current step.
   int cu_hh = it0_hh, cu_t = it0_tile;
-  const bool alibi = EXT && slopes != nullptr;
 
   // S = Q K^T of the tile in buffer `par` (P waves): rows 0-31 and 32-63; a lane owns key
   // kw + l32, register r holds row 32qs + 8(r/4) + 4g + r%4
@@ -428,7 +430,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           float p;
           if constexpr (EXT && MODE != 0) {
             const int diff = q0 + 32 * qs + 8 * rr + 4 * g + e - key;   // query - key
-            p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, s[qs][r] * c - lv[e]));
+            float x = s[qs][r] * c - lv[e];
+            if constexpr (ALIBI) x = __builtin_fmaf(__builtin_fabsf((float)diff), ab2, x);
+            p = __builtin_amdgcn_exp2f(x);
             if constexpr (MASK) {
               const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
               if (!vis) p = 0.f;
@@ -459,10 +463,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     if constexpr (EXT) {
       const int dmin = q0 - (k0 + kBwdKeys - 1), dmax = q0 + kBwdRows - 1 - k0;   // query - key
       const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
-      const float ab2 = alibi ? -slopes[kvh * G + cu_hh] * kLog2e : 0.f;
+      const float ab2 = ALIBI ? -slopes[kvh * G + cu_hh] * kLog2e : 0.f;
+      // two tile kinds: masked, and (inside the band) bias-only with ALiBi or plain without
       if (!inside) probs(st, q0, ab2, std::integral_constant<int, 1>{});
-      else if (alibi) probs(st, q0, ab2, std::integral_constant<int, 2>{});
-      else probs(st, q0, ab2, std::integral_constant<int, 0>{});
+      else probs(st, q0, ab2, std::integral_constant<int, ALIBI ? 2 : 0>{});
     } else if constexpr (CAUSAL) {
       if (cu_t < kDiag) probs(st, q0, 0.f, std::integral_constant<int, 1>{});
       else probs(st, q0, 0.f, std::integral_constant<int, 0>{});
@@ -661,7 +665,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restri
 // VARLEN: packed sequences as in bwd_pre_kernel; a query block past its sequence's end exits at
 // once.  EXT: window and ALiBi as in the dK/dV kernel; key tiles outside the block's band are
 // skipped and every other tile takes the masked path with the bias.
-template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, int ROWS = kDqRows>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN = false, bool EXT = false, int ROWS = kDqRows,
+          bool ALIBI = false>
 __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dsum, const float* __restrict__ Lse2,
@@ -740,12 +745,14 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) off_tr[db][hh] = tr_off<D>(lane, db, hh);
-  uint32_t dma_kv[PW];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int pch = 64 * (NW * i + w) + lane;
+  // piece NW i + w holds rows 64 NW i / CH further on than piece w, with the same swizzle (a
+  // multiple of 16 rows), so its source is dma_kv + i * 64 NW / CH rows, a uniform offset
+  static_assert((64 * NW / CH) % 16 == 0, "pieces of one wave keep the row swizzle");
+  uint32_t dma_kv;
+  {
+    const int pch = 64 * w + lane;
     const int r = pch / CH, cc = pch % CH;
-    dma_kv[i] = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
+    dma_kv = ((uint32_t)r * D + ((cc ^ swz<D>(r)) << 3)) * 2;
   }
   auto load_tiles = [&](int j, auto par) __attribute__((always_inline)) {
     short* kv = KV(par);
@@ -753,14 +760,15 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int piece = NW * i + w;
-      buffer_load16_lds(krs, kv + 512 * piece, dma_kv[i] + rowoff);
-      buffer_load16_lds(vrs, kv + TILE + 512 * piece, dma_kv[i] + rowoff);
+      const uint32_t soff = rowoff + (uint32_t)i * (64 * NW / CH) * D * 2;
+      buffer_load16_lds(krs, kv + 512 * piece, dma_kv, soff);
+      buffer_load16_lds(vrs, kv + TILE + 512 * piece, dma_kv, soff);
     }
   };
 
   // window (0: none; capped at N, which already sees everything) and ALiBi slope in log2 units
   const int W = (EXT && window > 0) ? min(window, N) : 0;
-  const float ab2 = (EXT && slopes != nullptr) ? -slopes[h] * kLog2e : 0.f;
+  const float ab2 = ALIBI ? -slopes[h] * kLog2e : 0.f;
   const int kend = CAUSAL ? min(N, q0 + ROWS) : (W > 0 ? min(N, q0 + ROWS + W - 1) : N);
   const int ntiles = (kend + kDqKeys - 1) / kDqKeys;
   // first tile with a key inside the window of the block's first row
@@ -798,7 +806,9 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
       float p;
       if constexpr (EXT && MODE != 0) {
         const int diff = qrow - (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3));   // query - key
-        p = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf((float)diff), ab2, st[r] * c - lse2));
+        float x = st[r] * c - lse2;
+        if constexpr (ALIBI) x = __builtin_fmaf(__builtin_fabsf((float)diff), ab2, x);
+        p = __builtin_amdgcn_exp2f(x);
         if constexpr (MASK) {
           const bool vis = (CAUSAL ? diff >= 0 : (W == 0 || diff > -W)) && (W == 0 || diff < W);
           if (!vis) p = 0.f;
@@ -899,23 +909,20 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   };
   if constexpr (EXT) {
     // tiles that cross a window edge or the diagonal for this wave's rows take the masked path,
-    // tiles wholly inside the band the bias-only (ALiBi) or plain path
-    using Mode0 = std::integral_constant<int, 0>;
+    // tiles wholly inside the band the bias-only path with ALiBi, the plain path without (two
+    // tile kinds per kernel)
     using Mode1 = std::integral_constant<int, 1>;
-    using Mode2 = std::integral_constant<int, 2>;
-    const bool alibi = slopes != nullptr;
+    using Inner = std::integral_constant<int, ALIBI ? 2 : 0>;
     for (; j < jact; ++j) {
       const int kt0 = j * kDqKeys;
       const int dmin = qw - (kt0 + kDqKeys - 1), dmax = qw + 31 - kt0;   // query - key
       const bool inside = (CAUSAL ? dmin >= 0 : (W == 0 || dmin > -W)) && (W == 0 || dmax < W);
       if (j & 1) {
         if (!inside) step(j, Par1{}, Mode1{});
-        else if (alibi) step(j, Par1{}, Mode2{});
-        else step(j, Par1{}, Mode0{});
+        else step(j, Par1{}, Inner{});
       } else {
         if (!inside) step(j, Par0{}, Mode1{});
-        else if (alibi) step(j, Par0{}, Mode2{});
-        else step(j, Par0{}, Mode0{});
+        else step(j, Par0{}, Inner{});
       }
     }
   } else {
@@ -948,7 +955,7 @@ static hipError_t launch_pre_t(const void* q, const void* k, const void* o, cons
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false, bool ALIBI = false>
 static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 void* dk, void* dv, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu,
                                 float scale, bool out32, const void* workspace, hipStream_t stream, int window = 0,
@@ -958,7 +965,7 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
   const BwdWs w = bwd_ws(const_cast<void*>(workspace), B, Hq, rows);
   const int nkb = (rows + kBwdKeys - 1) / kBwdKeys;
   const int ns = (VARLEN || EXT) ? 1 : dkdv_splits(B, Hq, Hkv, N);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nkb * B * Hkv * ns), dim3(512), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL, VARLEN, EXT, ALIBI>), dim3(nkb * B * Hkv * ns), dim3(512), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                      w.dsum, w.lse2, dk, dv, Hq, Hkv, N, w.npad, nkb, scale * kLog2e, scale, cu, window,
                      slopes, (int)out32, ns > 1 ? w.part : (float*)nullptr, ns);
@@ -971,7 +978,7 @@ static hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, con
   return hipGetLastError();
 }
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT = false, bool ALIBI = false>
 static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               void* dq, int B, int Hq, int Hkv, int N, int max_seqlen, const int* cu, float scale,
                               bool out32, const void* workspace, hipStream_t stream, int window = 0,
@@ -994,7 +1001,8 @@ static hipError_t launch_dq_t(const void* q, const void* k, const void* v, const
     }
   }
   const int nqb = (rows + kDqRows - 1) / kDqRows;
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT>), dim3(nqb * BH), dim3(kDqRows / 32 * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL, VARLEN, EXT, kDqRows, ALIBI>), dim3(nqb * BH),
+                     dim3(kDqRows / 32 * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                      w.dsum, w.lse2, dq, Hq, Hkv, N, w.npad, BH, nqb, scale * kLog2e, scale, cu, window,
                      slopes, (int)out32);
@@ -1057,15 +1065,21 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
 static hipError_t launch_dkdv_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                     void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, bool out32,
                                     const void* workspace, hipStream_t stream, int window, const float* slopes) {
-  return launch_dkdv_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, nullptr, scale,
-                                                      out32, workspace, stream, window, slopes);
+  if (slopes != nullptr)
+    return launch_dkdv_t<BF16, D, CAUSAL, false, true, true>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, nullptr,
+                                                             scale, out32, workspace, stream, window, slopes);
+  return launch_dkdv_t<BF16, D, CAUSAL, false, true, false>(q, k, v, dout, lse, dk, dv, B, Hq, Hkv, N, N, nullptr,
+                                                            scale, out32, workspace, stream, window, slopes);
 }
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool EXT_ = true>
 static hipError_t launch_dq_ext_t(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                   void* dq, int B, int Hq, int Hkv, int N, float scale, bool out32,
                                   const void* workspace, hipStream_t stream, int window, const float* slopes) {
-  return launch_dq_t<BF16, D, CAUSAL, false, true>(q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, nullptr, scale,
-                                                    out32, workspace, stream, window, slopes);
+  if (slopes != nullptr)
+    return launch_dq_t<BF16, D, CAUSAL, false, true, true>(q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, nullptr, scale,
+                                                           out32, workspace, stream, window, slopes);
+  return launch_dq_t<BF16, D, CAUSAL, false, true, false>(q, k, v, dout, lse, dq, B, Hq, Hkv, N, N, nullptr, scale,
+                                                          out32, workspace, stream, window, slopes);
 }
 
 hipError_t launch_bwd_dkdv_ext(const void* q, const void* k, const void* v, const void* dout, const float* lse,

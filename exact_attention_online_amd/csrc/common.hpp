@@ -161,6 +161,12 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, short* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)off, 0, 0, 0);
 }
+// The same with a uniform byte offset `soff` (a scalar register) added to the lane's `off`, so
+// that loads whose lane offsets differ by a uniform amount share one address register.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, short* dst, uint32_t off, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)off, (int)soff, 0,
+                                           0);
+}
 
 // Wait for every outstanding memory operation.  Issued once after the loads of loop-invariant
 // operands: without it the counter-based waits the compiler places inside the loop (it cannot

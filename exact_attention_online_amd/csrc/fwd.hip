@@ -166,19 +166,22 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   // K/V of this head through bounds-checked buffer loads: keys >= N read as zeros
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, (uint32_t)N * D * 2);
-  // direct loads: piece p = 4i + w of a tile; lane l fills LDS chunk 64p + l (row (64p + l) / CH,
+  // direct loads: piece p = NWV i + w of a tile; lane l fills LDS chunk 64p + l (row (64p + l) / CH,
   // physical chunk l % CH) with the logical chunk that the swizzle puts there
-  uint32_t goff[T::PIECES / NWV];
-#pragma unroll
-  for (int i = 0; i < T::PIECES / NWV; ++i) {
-    const int p = 64 * (NWV * i + w) + lane;
+  // (piece NWV i + w lies 64 NWV i / CH rows after piece w, a multiple of the swizzle's period,
+  // so its source is goff plus a uniform offset)
+  static_assert((64 * NWV / CH) % 16 == 0, "pieces of one wave keep the row swizzle");
+  uint32_t goff;
+  {
+    const int p = 64 * w + lane;
     const int row = p / CH, pch = p % CH;
-    goff[i] = ((uint32_t)row * D + ((pch ^ swz<D>(row)) << 3)) * 2;
+    goff = ((uint32_t)row * D + ((pch ^ swz<D>(row)) << 3)) * 2;
   }
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, short* dst, int kt0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < T::PIECES / NWV; ++i)
-      buffer_load16_lds(rs, dst + 512 * (NWV * i + w), goff[i] + (uint32_t)kt0 * D * 2);
+      buffer_load16_lds(rs, dst + 512 * (NWV * i + w), goff,
+                        (uint32_t)kt0 * D * 2 + (uint32_t)i * (64 * NWV / CH) * D * 2);
   };
 
   // loop-invariant LDS offsets (16-bit units): K rows l32 (+32 kb) at chunk 2kk + g; V^T
