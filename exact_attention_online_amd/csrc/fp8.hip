@@ -152,9 +152,11 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 // The same with the A operand scaled by 2^(sa - 127) (an E8M0 exponent, 0 <= sa <= 254, the same
-// in every lane): the product is exact, as for any power of two.
-__device__ __forceinline__ f32x16_t mfma_fp8_sa(const i32x8_t& a, const i32x8_t& b, f32x16_t c, int sa) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+// in every lane) and each lane's 32 B values by 2^(sb - 127) (an E8M0 exponent per lane; in
+// O^T += V^T P^T a lane's B values belong to one query): the products are exact, as for any
+// power of two.
+__device__ __forceinline__ f32x16_t mfma_fp8_s(const i32x8_t& a, const i32x8_t& b, f32x16_t c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // Index (bytes) of byte `col` of row `row` in a V tile of 128-byte rows, 16-byte chunks
@@ -175,9 +177,12 @@ __device__ __forceinline__ int fp8_key_of_row(int rho) {
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + i;
 }
 
-// Headroom (log2 units) of the deferred rescaling: a row keeps its maximum until a score
-// passes it by more than this, so the probabilities against the kept maximum stay <= 2^1.
+// Headroom (log2 units) of the probabilities' reference: a row keeps it until a score passes it
+// by more than this, so the probabilities against it stay <= 2^1.
 constexpr float kFp8Stale = 1.0f;
+// Largest power-of-two offset (log2 units) between a row's reference for its probabilities and
+// the accumulator's reference maximum before the accumulator is rebased (see fwd_fp8_kernel).
+constexpr int kFp8MaxShift = 64;
 // log2 of the factor applied to the probabilities before their e4m3 conversion: probabilities
 // <= 2^kFp8Stale then map to <= 2^8 (e4m3 holds up to 448), and values down to 2^-13 of the kept
 // maximum stay in the normal range (e4m3 normals start at 2^-6).
@@ -192,10 +197,16 @@ constexpr int kFp8Ones = 0x38383838;
 // block with the exponentials and P V MFMAs of tile j.
 //
 // Scales.  S^T = K Q^T is in code units; ceff = scale * log2(e) * qscale * kscale of the tile's
-// 128-key block multiplies it inside the exponent.  The probabilities are formed against a row
-// maximum kept until a score passes it by more than kFp8Stale (rescaling on growth, as in
-// attn_fwd_kernel), times 2^kFp8Pre, and converted to e4m3; they carry no block scale, so the
-// largest ones stay exact.  The accumulator is kept in a unit u (a V block scale): a block whose
+// 128-key block multiplies it inside the exponent.  The accumulator and the row sums are kept
+// against a reference maximum m (per row, the row's first finite maximum).  The probabilities
+// are formed against m + kx, kx an integer offset kept until a score passes m + kx by more than
+// kFp8Stale, times 2^kFp8Pre, and converted to e4m3; they carry no block scale, so the largest
+// ones stay exact.  When a row's maximum grows, kx rises to the least integer that brings it
+// within kFp8Stale, and the P V and row-sum MFMAs multiply that row's probabilities by 2^kx
+// through the B operand's per-lane E8M0 scale: the accumulator is never multiplied for a grown
+// maximum (the online softmax's rescale of the accumulator, applied to the new terms instead,
+// exactly).  Only a row whose offset passes kFp8MaxShift is rebased (acc, row sum *= 2^-kx,
+// m += kx, kx = 0; exact as well).  The accumulator is kept in a unit u (a V block scale): a block whose
 // scale is u times a power of two (power-of-two block scales, attn_fp8_prep's pow2_scale) enters
 // through the A-operand scale of its P V MFMAs, exactly and without vector work; otherwise, at
 // the block's first tile, the accumulator is multiplied by u / vscale (with the rescale factor of
@@ -269,7 +280,8 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
   // (every register of a lane ends up holding its query's sum): the sum costs no vector ALU work
   f32x16_t lacc = f32x16_t{};
   const i32x8_t ones = {kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
-  float m = -INFINITY;
+  float m = -INFINITY;         // reference maximum of the accumulator and row sums (log2 units)
+  int kx = 0;                  // offset of the probabilities' reference: m + kx
   float vs_cur = vs_head[0];   // the accumulator's unit: the V scale of the last block added
 
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
@@ -381,29 +393,50 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
     // scale; otherwise the accumulator changes unit (vs_cur -> this block's scale).
     bool vres = false;
     if constexpr (BSTART) {
-      const uint32_t rb = __float_as_uint(vs_t / vs_cur);
-      const uint32_t ef = (rb >> 23) & 0xFFu;
-      if ((rb & 0x7FFFFFu) == 0u && ef >= 1u && ef <= 254u) {
-        sa = (int)ef;          // E8M0 exponent of the ratio
+      // vs_t / vs_cur is a power of two exactly when the two (normal) scales share their
+      // mantissa; its E8M0 exponent is then 127 + the difference of their exponents
+      const uint32_t bt = __float_as_uint(vs_t), bc = __float_as_uint(vs_cur);
+      const int et = (int)((bt >> 23) & 0xFFu), ec = (int)((bc >> 23) & 0xFFu);
+      const int ef = 127 + et - ec;
+      if (((bt ^ bc) & 0x807FFFFFu) == 0u && et >= 1 && et <= 254 && ec >= 1 && ec <= 254 && ef >= 1 && ef <= 254) {
+        sa = ef;
       } else {
         vres = true;
         sa = 127;
       }
     }
-    // deferred rescale, per row, as in attn_fwd_kernel
-    const bool grow = mt > m + kFp8Stale;
-    const bool any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
-    if (vres || any_grow) {
-      float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-      asm volatile("" : "+v"(alpha));
-      m = grow ? mt : m;
-      const float f = vres ? alpha * (vs_cur / vs_t) : alpha;
+    // a row whose maximum passes m + kx + kFp8Stale raises kx (the first finite maximum sets m)
+    const bool grow = mt > m + (float)kx + kFp8Stale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      if (grow) {
+        if (m == -INFINITY) {
+          m = mt;
+        } else {
+          kx = (int)__builtin_ceilf(mt - kFp8Stale - m);
+        }
+      }
+      const bool rebase = kx > kFp8MaxShift;
+      if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
+        float f = rebase ? __builtin_ldexpf(1.f, -kx) : 1.f;
+        asm volatile("" : "+v"(f));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= f;
+        lacc *= f;
+        if (rebase) {
+          m += (float)kx;
+          kx = 0;
+        }
+      }
+    }
+    if (vres) {
+      // a V block scale that is not a power of two times the accumulator's unit
+      const float f = vs_cur / vs_t;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= f;
-      if (any_grow) lacc *= alpha;
-      if (vres) vs_cur = vs_t;
+      vs_cur = vs_t;
     }
-    const float mo = ((m == -INFINITY) ? 0.f : m) - kFp8Pre;
+    const float mo = ((m == -INFINITY) ? 0.f : m + (float)kx) - kFp8Pre;
+    const int sb = 127 + kx;   // E8M0 exponent 2^kx of this lane's probabilities
     // S^T of the next tile (past the wave's last tile it reads a stale buffer; never used)
     compute_s(Other{}, sn);
     int pw[8];
@@ -421,7 +454,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
       }
     // B operand (P^T): slot e = 16kb + r  ->  key 32kb + 16(r/8) + 8g + (r%8)
     const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    lacc = mfma_fp8(ones, pb, lacc);
+    lacc = mfma_fp8_s(ones, pb, lacc, 127, sb);
     const uint8_t* Vb = Vs(par);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -434,7 +467,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
         av[2 * t + 1] = x[1];
       }
       const i32x8_t a = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-      o[db] = mfma_fp8_sa(a, pb, o[db], sa);
+      o[db] = mfma_fp8_s(a, pb, o[db], sa, sb);
     }
     ceff = cq * ks_n;
     vs_t = vs_n;
