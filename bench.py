@@ -34,6 +34,9 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 
 METRIC = "attention fwd / fwd+bwd TFLOPs/s (bf16, N=16k, d=128) + % of MFMA peak"
 WORKLOAD = "long_bf16"
 SEED = 3
+# An idle GPU's engine clock ramps up over roughly the first 0.1 s of load: a workload whose step
+# takes well under a millisecond needs hundreds of warm-up steps before its steady rate shows.
+WARMUP_SECONDS = 0.25
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_long_bf16_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_online_amd", "csrc", f) for f in ("bwd.hip", "common.hpp")]
 
@@ -42,7 +45,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3, and as many as fill %.1f s of GPU time)"
+                         % WARMUP_SECONDS)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -55,6 +60,29 @@ def parse():
                     help="before the warmup, run one plain device-to-device copy of MIB MiB (a kernel of "
                          "known traffic that scales HBM byte counters read under a profiler)")
     return ap.parse_args()
+
+
+def warm_up(step, args) -> int:
+    """Run the untimed warm-up and return how many steps it took: args.warmup steps when given,
+    else at least 3 and as many more as fill WARMUP_SECONDS of GPU time (batches of doubling
+    size, each followed by a synchronisation)."""
+    import torch
+
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n, batch = 0, 3
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(batch):
+            step()
+        n += batch
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARMUP_SECONDS:
+            return n
+        batch = min(2 * batch, 128)
 
 
 def kernel_source_hash() -> str:
@@ -228,8 +256,7 @@ def bench_decode(args):
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     ws = torch.empty(eao.splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, 0), dtype=torch.uint8,
                      device=dev)
-    for _ in range(args.warmup):
-        eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse)
+    nwarm = warm_up(lambda: eao.fwd_splitkv(q, k, v, w.causal, w.scale, 0, ws, o, lse), args)
     steps = max(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -275,7 +302,7 @@ def bench_decode(args):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -342,9 +369,7 @@ def bench_window(args, with_bwd=False):
             if evs is not None:
                 evs[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -368,7 +393,7 @@ def bench_window(args, with_bwd=False):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -420,9 +445,9 @@ def bench_ablation(args):
     lib = eao.load()
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nwarm = 0
     for causal in (True, False):
-        for _ in range(args.warmup):
-            eao.fwd(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        nwarm += warm_up(lambda: eao.fwd(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse), args)
         call_args = (P(q), P(k), P(v), P(o), P(lse), w.B, w.Hq, w.Hkv, w.N, w.d, int(causal), w.scale, eao.BF16,
                      None, None, None, stream)
         torch.cuda.synchronize()
@@ -449,8 +474,7 @@ def bench_ablation(args):
     sq, sk, sv = (round_to(x, w.dtype).to(dev).contiguous() for x in (s32, t32, u32))
     so = torch.empty_like(sq)
     slse = torch.empty((1, w.Hq, w.N), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        eao.fwd(sq, sk, sv, causal=True, scale=w.scale, out=so, lse=slse)
+    nwarm += warm_up(lambda: eao.fwd(sq, sk, sv, causal=True, scale=w.scale, out=so, lse=slse), args)
     small_args = (P(sq), P(sk), P(sv), P(so), P(slse), 1, w.Hq, w.Hkv, w.N, w.d, 1, w.scale, eao.BF16, None, None,
                   None, stream)
     torch.cuda.synchronize()
@@ -472,7 +496,7 @@ def bench_ablation(args):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(tot_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -523,10 +547,8 @@ def bench_fp8(args):
     (q8, qs), (k8, ks), (v8, vs) = prep()
     o = torch.empty(w.B, w.Hq, w.N, w.d, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(w.B, w.Hq, w.N, dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        eao.fwd_fp8(q8, k8, v8, qs, ks, vs, w.causal, w.scale, o, lse)
-        prep()
-    torch.cuda.synchronize()
+    nwarm = warm_up(lambda: eao.fwd_fp8(q8, k8, v8, qs, ks, vs, w.causal, w.scale, o, lse), args)
+    nwarm += warm_up(prep, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -555,7 +577,7 @@ def bench_fp8(args):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -622,9 +644,7 @@ def bench_varlen(args, with_bwd=False):
             if evs is not None:
                 evs[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -647,7 +667,7 @@ def bench_varlen(args, with_bwd=False):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -738,9 +758,7 @@ def main():
               file=sys.stderr, flush=True)
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -774,7 +792,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -13,13 +13,13 @@
 //     h >= 8 across lanes (shuffles), exactly in the order of the definition so the codes are
 //     reproducible bit for bit; then a workgroup max of |y|, scale = amax / 448, and
 //     v_cvt_pk_fp8_f32 (round to nearest even) of y / scale.  HBM-bound: 4 bytes in, 1 out.
-//   * fwd_fp8_kernel: the forward of fwd.hip (same grid, direct loads, K one tile ahead of V,
-//     deferred rescaling) on v_mfma_scale_f32_32x32x64_f8f6f4 (scales 1).  S^T = K Q^T with the
-//     Q and K descales folded into the exp2 argument (one scalar per tile pair); the V block
-//     scale is folded into the exponent too (relative to the head's largest V scale), so the
-//     accumulator never needs rescaling when the V block changes.  The probabilities are
-//     multiplied by 2^7 before their e4m3 conversion (keeps small probabilities out of the
-//     subnormal range) and O^T += V^T P^T runs in fp8 as well.
+//   * fwd_fp8_kernel: the forward of fwd.hip (same grid, direct loads, deferred rescaling) on
+//     v_mfma_scale_f32_32x32x64_f8f6f4.  S^T = K Q^T with the Q and K descales folded into the
+//     exp2 argument (one scalar per tile pair); power-of-two V block scales and the offsets of
+//     grown row maxima enter exactly through the MFMA's E8M0 scale operands, so the accumulator
+//     is multiplied only in rare cases.  The probabilities are multiplied by 2^7 before their
+//     e4m3 conversion (keeps small probabilities out of the subnormal range) and
+//     O^T += V^T P^T runs in fp8 as well, one tile behind S^T so the two overlap.
 //     K rows are placed in LDS in a permuted order inside each 32-row block (row 8a + 4g + i
 //     holds key 16(a/2) + 8g + 4(a%2) + i), so each lane's accumulator registers cover runs of
 //     8 consecutive keys; ds_read_b64_tr_b8 on the naturally ordered V tile then yields V^T
@@ -159,6 +159,10 @@ __device__ __forceinline__ f32x16_t mfma_fp8_s(const i32x8_t& a, const i32x8_t& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// Larger of two scores (finite or -inf): the NaN-propagating maximum, which gfx950 does in one
+// v_maximum3_f32 without first quieting its operands (fmaxf's IEEE form needs that per operand).
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Index (bytes) of byte `col` of row `row` in a V tile of 128-byte rows, 16-byte chunks
 // XOR-swizzled by row % 8: the transposed 8-byte reads of 8 consecutive rows x 2 chunks hit 16
 // distinct 16-byte bank groups.
@@ -193,8 +197,12 @@ constexpr int kFp8Ones = 0x38383838;
 // One workgroup per (batch, query head, block of NWV * 32 query rows), 32 rows per wave: 8 waves
 // (256 rows) when that gives every CU two or more workgroups, else 4.  Structure of
 // attn_fwd_kernel (fwd.hip): K and V tiles of 64 keys go straight from HBM into double-buffered
-// LDS with direct loads, K one tile ahead of V, and the S^T MFMAs of tile j + 1 share a basic
-// block with the exponentials and P V MFMAs of tile j.
+// LDS with direct loads.  Three streams of work share one basic block per tile j: the S^T
+// MFMAs of tile j + 1, the exponentials and conversions of tile j, and the P V and row-sum
+// MFMAs of tile j - 1 (its probabilities wait one tile in registers, its V tile one tile in
+// LDS).  Neither MFMA stream depends on the vector work beside it, so the matrix cores and
+// the vector ALU of a SIMD stay busy together instead of taking turns.  K is loaded two tiles
+// ahead, V in the iteration of its own tile (it is read one iteration later).
 //
 // Scales.  S^T = K Q^T is in code units; ceff = scale * log2(e) * qscale * kscale of the tile's
 // 128-key block multiplies it inside the exponent.  The accumulator and the row sums are kept
@@ -206,13 +214,16 @@ constexpr int kFp8Ones = 0x38383838;
 // through the B operand's per-lane E8M0 scale: the accumulator is never multiplied for a grown
 // maximum (the online softmax's rescale of the accumulator, applied to the new terms instead,
 // exactly).  Only a row whose offset passes kFp8MaxShift is rebased (acc, row sum *= 2^-kx,
-// m += kx, kx = 0; exact as well).  The accumulator is kept in a unit u (a V block scale): a block whose
-// scale is u times a power of two (power-of-two block scales, attn_fp8_prep's pow2_scale) enters
-// through the A-operand scale of its P V MFMAs, exactly and without vector work; otherwise, at
-// the block's first tile, the accumulator is multiplied by u / vscale (with the rescale factor of
-// a grown maximum, if any) and u becomes that block's scale.  The row sums come from one more
-// MFMA per tile against an all-ones operand, i.e. over the same e4m3 probabilities that enter
-// the accumulator.  The per-tile scales are read one tile ahead with uniform (scalar) loads.
+// m += kx, kx = 0; exact as well), after the P V of the previous tile has entered.  The
+// accumulator is kept in a unit u (a V block scale): a block whose scale is u times a power of
+// two (power-of-two block scales, attn_fp8_prep's pow2_scale) enters through the A-operand
+// scale of its P V MFMAs, exactly and without vector work; otherwise, at the block's first tile,
+// the accumulator is multiplied by u / vscale and u becomes that block's scale.  The row sums
+// come from one more MFMA per tile against an all-ones operand, i.e. over the same e4m3
+// probabilities that enter the accumulator; its per-lane B scale is the same 2^kx.  (A 16x16x128
+// MFMA would take half the matrix cycles, but its scale blocks of 32 keys each span two lane
+// groups, which hold different queries here, so rows with different offsets would mix.)  The
+// per-tile scales are read one tile ahead with uniform (scalar) loads.
 // Epilogue: O = acc * u * 2^-kFp8Pre / l, LSE = ln 2 * (m + log2 l).
 template <bool CAUSAL, int NWV>
 __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
@@ -279,9 +290,15 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
   // row sums of the e4m3 probabilities, from one more MFMA per tile with an all-ones A operand
   // (every register of a lane ends up holding its query's sum): the sum costs no vector ALU work
   f32x16_t lacc = f32x16_t{};
-  const i32x8_t ones = {kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
-  float m = -INFINITY;         // reference maximum of the accumulator and row sums (log2 units)
-  int kx = 0;                  // offset of the probabilities' reference: m + kx
+  // the all-ones operand sits in LDS and is read for each tile: two LDS reads instead of the
+  // eight register moves that rematerialise it when registers are scarce
+  __shared__ __attribute__((aligned(32))) int ones_lds[8];
+  if (tid < 8) ones_lds[tid] = kFp8Ones;
+  // Per row: m, the reference maximum of the accumulator and the row sums (log2 units), set by
+  // the first tile, which always holds a visible key (key 0: causal rows start there, and N >= 1);
+  // kxf, the integer offset of the probabilities' reference m + kxf; mstale = m + kFp8Stale and
+  // mpre = m - kFp8Pre, which change only with m.
+  float m = 0.f, kxf = 0.f, mstale = 0.f, mpre = 0.f;
   float vs_cur = vs_head[0];   // the accumulator's unit: the V scale of the last block added
 
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
@@ -342,16 +359,38 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
       }
     }
   };
-  // staging of one iteration (tile j lives in the buffers of parity j % 2): K_{j+2} replaces
-  // K_j, V_{j+1} replaces V_{j-1}
+  // staging of iteration j (tile j lives in the buffers of parity j % 2): K_{j+2} replaces K_j
+  // (read for S^T in iteration j - 1), V_j replaces V_{j-2} (read in iteration j - 1)
   auto stage = [&](int j, auto par) __attribute__((always_inline)) {
-    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
     if (j + 2 < ntiles) load_k(Ks(par), (j + 2) * BC);
-    if (j + 1 < ntiles) load_v(Vs(Other{}), (j + 1) * BC);
+    load_v(Vs(par), j * BC);
   };
   auto publish = [&]() __attribute__((always_inline)) {
     wait_all_loads();
     __syncthreads();
+  };
+
+  // probabilities of the previous tile (P^T operand) and the E8M0 scales of their MFMAs
+  i32x8_t pb_prev = {0, 0, 0, 0, 0, 0, 0, 0};
+  int sa_prev = 127, sb_prev = 127;
+  // O^T += V^T P^T and the row sums for the previous tile, whose V tile is in buffer `ppar`
+  auto pv_prev = [&](auto ppar) __attribute__((always_inline)) {
+    const i32x8_t ones = *(const i32x8_t*)ones_lds;
+    lacc = mfma_fp8_s(ones, pb_prev, lacc, 127, sb_prev);
+    const uint8_t* Vb = Vs(ppar);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      int av[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // 8 consecutive keys 16t + 8g .. +7 at column d = 32db + l32
+        const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(Vb + 16 * t * D + off_v[db]));
+        av[2 * t] = x[0];
+        av[2 * t + 1] = x[1];
+      }
+      const i32x8_t a = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+      o[db] = mfma_fp8_s(a, pb_prev, o[db], sa_prev, sb_prev);
+    }
   };
 
   f32x16_t sA[2], sB[2];   // S^T of even / odd tiles
@@ -359,10 +398,12 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
   // E8M0 scale of the P V MFMAs of the current V block (127 = 2^0)
   float ceff = cq * ks_head[0], vs_t = vs_cur;
   int sa = 127;
-  // BSTART: the tile starts a 128-key block (tiles are 64 keys: even tiles)
-  auto body = [&](int j, auto par, auto mask_tag, auto bstart_tag) __attribute__((always_inline)) {
+  // BSTART: the tile starts a 128-key block (tiles are 64 keys: even tiles); FIRST: tile 0 (no
+  // previous tile)
+  auto body = [&](int j, auto par, auto mask_tag, auto bstart_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool BSTART = decltype(bstart_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     constexpr int P = decltype(par)::value;
     using Other = std::integral_constant<int, 1 - P>;
     auto& sc = P == 0 ? sA : sB;
@@ -382,15 +423,22 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
           if (key >= N || (CAUSAL && key > qrow)) sc[kb][r] = -INFINITY;
         }
     }
-    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // four chains of eight scores, each step folding two new ones (one three-input maximum)
+    float mx4[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[kb][r]);
-    const float mt = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * ceff;
+    for (int e = 0; e < 4; ++e) {
+      mx4[e] = smax(sc[0][e], sc[0][e + 4]);
+      mx4[e] = smax(smax(mx4[e], sc[0][e + 8]), sc[0][e + 12]);
+      mx4[e] = smax(smax(mx4[e], sc[1][e]), sc[1][e + 4]);
+      mx4[e] = smax(smax(mx4[e], sc[1][e + 8]), sc[1][e + 12]);
+    }
+    const float mh = smax(smax(smax(mx4[0], mx4[1]), mx4[2]), mx4[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
+    const float mt = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * ceff;
     // A new V block: when its scale is an exact power of two times the accumulator's unit
     // (power-of-two block scales), the P V MFMAs apply that factor through their A-operand
-    // scale; otherwise the accumulator changes unit (vs_cur -> this block's scale).
+    // scale; otherwise the accumulator changes unit (vs_cur -> this block's scale) once the
+    // previous tile's P V has entered.
     bool vres = false;
     if constexpr (BSTART) {
       // vs_t / vs_cur is a power of two exactly when the two (normal) scales share their
@@ -405,38 +453,17 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
         sa = 127;
       }
     }
-    // a row whose maximum passes m + kx + kFp8Stale raises kx (the first finite maximum sets m)
-    const bool grow = mt > m + (float)kx + kFp8Stale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      if (grow) {
-        if (m == -INFINITY) {
-          m = mt;
-        } else {
-          kx = (int)__builtin_ceilf(mt - kFp8Stale - m);
-        }
-      }
-      const bool rebase = kx > kFp8MaxShift;
-      if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
-        float f = rebase ? __builtin_ldexpf(1.f, -kx) : 1.f;
-        asm volatile("" : "+v"(f));
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= f;
-        lacc *= f;
-        if (rebase) {
-          m += (float)kx;
-          kx = 0;
-        }
-      }
+    if constexpr (FIRST) {
+      // the first tile sets the reference (finite: the tile holds a visible key for every row)
+      m = (mt == -INFINITY) ? 0.f : mt;
+      mstale = m + kFp8Stale;
+      mpre = m - kFp8Pre;
+    } else {
+      // a row whose maximum passes m + kxf + kFp8Stale raises kxf to the least integer that
+      // brings it back within (a fully masked row: ceil(-inf) leaves kxf)
+      kxf = smax(kxf, __builtin_ceilf(mt - mstale));
     }
-    if (vres) {
-      // a V block scale that is not a power of two times the accumulator's unit
-      const float f = vs_cur / vs_t;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= f;
-      vs_cur = vs_t;
-    }
-    const float mo = ((m == -INFINITY) ? 0.f : m + (float)kx) - kFp8Pre;
-    const int sb = 127 + kx;   // E8M0 exponent 2^kx of this lane's probabilities
+    const float mo = mpre + kxf;
     // S^T of the next tile (past the wave's last tile it reads a stale buffer; never used)
     compute_s(Other{}, sn);
     int pw[8];
@@ -452,23 +479,38 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
         const int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
         pw[(16 * kb + r) / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
       }
-    // B operand (P^T): slot e = 16kb + r  ->  key 32kb + 16(r/8) + 8g + (r%8)
+    // P V of the previous tile (its V tile is in the other buffer)
+    if constexpr (!FIRST) pv_prev(Other{});
+    // the new probabilities and the next S^T are due here: this keeps their exponentials and
+    // MFMAs in one block with the P V MFMAs above instead of letting them sink below the
+    // branches that follow
     const i32x8_t pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    lacc = mfma_fp8_s(ones, pb, lacc, 127, sb);
-    const uint8_t* Vb = Vs(par);
+    asm volatile("" ::"v"(pb), "v"(sn[0]), "v"(sn[1]));
+    // the rare rescales, now that the previous tile's terms are in: a rebase of rows whose
+    // offset passed kFp8MaxShift, a V block scale that is not a power of two times the unit
+    const bool rebase = kxf > (float)kFp8MaxShift;
+    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
+      float f = rebase ? __builtin_ldexpf(1.f, -(int)kxf) : 1.f;
+      asm volatile("" : "+v"(f));
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      int av[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // 8 consecutive keys 16t + 8g .. +7 at column d = 32db + l32
-        const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(Vb + 16 * t * D + off_v[db]));
-        av[2 * t] = x[0];
-        av[2 * t + 1] = x[1];
+      for (int db = 0; db < 4; ++db) o[db] *= f;
+      lacc *= f;
+      if (rebase) {
+        m += kxf;
+        kxf = 0.f;
+        mstale = m + kFp8Stale;
+        mpre = m - kFp8Pre;
       }
-      const i32x8_t a = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-      o[db] = mfma_fp8_s(a, pb, o[db], sa, sb);
     }
+    if (vres) {
+      const float f = vs_cur / vs_t;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= f;
+      vs_cur = vs_t;
+    }
+    sa_prev = sa;
+    sb_prev = 127 + (int)kxf;   // E8M0 exponent 2^kxf of this lane's probabilities
+    pb_prev = pb;
     ceff = cq * ks_n;
     vs_t = vs_n;
     publish();
@@ -479,9 +521,8 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
     publish();
   };
 
-  // prologue: K and V of tile 0, K of tile 1; S^T of tile 0
+  // prologue: K of tiles 0 and 1; S^T of tile 0
   load_k(Ks(Par0{}), 0);
-  load_v(Vs(Par0{}), 0);
   if (1 < ntiles) load_k(Ks(Par1{}), BC);
   publish();
   if (jact > 0) compute_s(Par0{}, sA);
@@ -494,17 +535,27 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
   using T_ = std::true_type;
   using F_ = std::false_type;
   int j = 0;
+  if (jact > 0) {
+    if (jmask > 0) body(0, Par0{}, F_{}, T_{}, T_{});
+    else body(0, Par0{}, T_{}, T_{}, T_{});
+    j = 1;
+  }
   for (; j + 2 <= jmask; j += 2) {
-    body(j, Par0{}, F_{}, T_{});
-    body(j + 1, Par1{}, F_{}, F_{});
+    body(j, Par1{}, F_{}, F_{}, F_{});
+    body(j + 1, Par0{}, F_{}, T_{}, F_{});
   }
   if (j < jmask) {
-    body(j, Par0{}, F_{}, T_{});
+    body(j, Par1{}, F_{}, F_{}, F_{});
     ++j;
   }
   for (; j < jact; ++j) {
-    if (j & 1) body(j, Par1{}, T_{}, F_{});
-    else body(j, Par0{}, T_{}, T_{});
+    if (j & 1) body(j, Par1{}, T_{}, F_{}, F_{});
+    else body(j, Par0{}, T_{}, T_{}, F_{});
+  }
+  // P V of the wave's last tile (its V tile was published by the last iteration)
+  if (jact > 0) {
+    if ((jact - 1) & 1) pv_prev(Par1{});
+    else pv_prev(Par0{});
   }
   for (; j < ntiles; ++j) idle(j);
 
