@@ -109,6 +109,31 @@ __device__ __forceinline__ float hi_to_float(uint32_t pair) {
   }
 }
 
+// Larger of two scores (finite or -inf): the NaN-propagating maximum, which gfx950 does in one
+// v_maximum3_f32 without first quieting its operands (fmaxf's IEEE form needs that per operand).
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Row maximum of the 16 x NK scores s[0..NK-1][0..15] a lane holds (registers r and r + 4 of one
+// block are the same column group): four chains, each step folding two new scores into one
+// three-input maximum, then the two lane halves.
+template <int NK>
+__device__ __forceinline__ float row_max(const f32x16_t (&s)[NK]) {
+  float mx[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    mx[e] = smax(s[0][e], s[0][e + 4]);
+    mx[e] = smax(smax(mx[e], s[0][e + 8]), s[0][e + 12]);
+#pragma unroll
+    for (int kb = 1; kb < NK; ++kb) {
+      mx[e] = smax(smax(mx[e], s[kb][e]), s[kb][e + 4]);
+      mx[e] = smax(smax(mx[e], s[kb][e + 8]), s[kb][e + 12]);
+    }
+  }
+  const float h = smax(smax(smax(mx[0], mx[1]), mx[2]), mx[3]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(h), __float_as_uint(h), false, false);
+  return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // max / sum of a value over lanes l and l ^ 32.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -159,10 +159,6 @@ __device__ __forceinline__ f32x16_t mfma_fp8_s(const i32x8_t& a, const i32x8_t& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// Larger of two scores (finite or -inf): the NaN-propagating maximum, which gfx950 does in one
-// v_maximum3_f32 without first quieting its operands (fmaxf's IEEE form needs that per operand).
-__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
 // Index (bytes) of byte `col` of row `row` in a V tile of 128-byte rows, 16-byte chunks
 // XOR-swizzled by row % 8: the transposed 8-byte reads of 8 consecutive rows x 2 chunks hit 16
 // distinct 16-byte bank groups.
@@ -423,18 +419,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
           if (key >= N || (CAUSAL && key > qrow)) sc[kb][r] = -INFINITY;
         }
     }
-    // four chains of eight scores, each step folding two new ones (one three-input maximum)
-    float mx4[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mx4[e] = smax(sc[0][e], sc[0][e + 4]);
-      mx4[e] = smax(smax(mx4[e], sc[0][e + 8]), sc[0][e + 12]);
-      mx4[e] = smax(smax(mx4[e], sc[1][e]), sc[1][e + 4]);
-      mx4[e] = smax(smax(mx4[e], sc[1][e + 8]), sc[1][e + 12]);
-    }
-    const float mh = smax(smax(smax(mx4[0], mx4[1]), mx4[2]), mx4[3]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
-    const float mt = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * ceff;
+    const float mt = row_max(sc) * ceff;
     // A new V block: when its scale is an exact power of two times the accumulator's unit
     // (power-of-two block scales), the P V MFMAs apply that factor through their A-operand
     // scale; otherwise the accumulator changes unit (vs_cur -> this block's scale) once the

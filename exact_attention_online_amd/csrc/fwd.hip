@@ -42,6 +42,10 @@ namespace eao {
 
 // Headroom (log2 units) of the deferred rescaling: probabilities stay <= 2^kStaleMax.
 constexpr float kStaleMax = 8.0f;
+// Running maximum of a row that has seen no visible key yet: finite and below any score, so the
+// first visible key always takes the rescale branch (its factor 2^(kMUnset - m) is 0) and the
+// exponentials need no test for an unset maximum (2^(-inf - kMUnset) = 0 for masked keys).
+constexpr float kMUnset = -1e30f;
 
 // LDS tiles (K and V, [BC keys][D], double-buffered each) are unpadded, with 16-byte chunks
 // XOR-swizzled by row (swz in common.hpp): a ds_read_b128 of 16 consecutive rows at one
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
   float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
+    m[qb] = kMUnset;
     l[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x16_t{};
@@ -252,7 +256,6 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
     const int kt0 = j * BC;
     stage(j, par);
     // ---- row maxima of tile j; rescale when a row's maximum has grown by more than kStaleMax
-    float muse[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if constexpr (EXT && MODE != 0) {
@@ -284,12 +287,7 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
             if (key >= N || (CAUSAL && key > qrow)) sc[qb][kb][r] = -INFINITY;
           }
       }
-      float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[qb][kb][r]);
-      const float mt = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * c;
+      const float mt = row_max(sc[qb]) * c;
       // The accumulator is rescaled only when some row's maximum has grown by more than
       // kStaleMax (log2 units) since the last rescale; otherwise the stale maximum is kept,
       // probabilities stay <= 2^kStaleMax, and the final division by l (computed against the
@@ -306,7 +304,6 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
       }
-      muse[qb] = (m[qb] == -INFINITY) ? 0.f : m[qb];
     }
     // ---- S^T of the next tile (past the wave's last tile it reads a stale buffer and the
     // result is never used), probabilities of tile j, O^T += V^T P^T
@@ -319,7 +316,7 @@ __global__ __launch_bounds__(NWV * 64, (EXT || NWV == 8) ? 1 : 2) void attn_fwd_
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[qb][kb][r] * c - muse[qb]);
+          const float p = __builtin_amdgcn_exp2f(sc[qb][kb][r] * c - m[qb]);
           sc[qb][kb][r] = p;
           rs4[r & 3] += p;
         }
