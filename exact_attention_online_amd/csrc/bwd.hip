@@ -215,7 +215,9 @@ __device__ __forceinline__ void store_row(void* __restrict__ base, size_t elem, 
 // each buffer a distinct LDS object).  Q and dO are read as 16-byte rows (A operands of S and
 // dP), Q^T and dO^T through transposed reads of the same tiles (A operands of dK^T and dV^T).
 // Two barriers per step: A (P of this tile written, next tile landed) and X (this tile's
-// buffer free for the loads of the tile three steps on).
+// buffer free for the loads of the tile three steps on).  Each half of a step holds the same
+// matrix work: before A the P wave's dV^T MFMAs (its own P needs no exchange) beside the dS
+// wave's dP MFMAs, after A the P wave's S MFMAs of the next tile beside the dS wave's dK^T.
 // VARLEN: packed sequences as in bwd_pre_kernel (K/V/dK/dV [Hkv,T,d], Q/dO [Hq,T,d]); a key block
 // past its sequence's end exits at once.
 // EXT: the sliding window and ALiBi bias of the forward with the same flag (key j visible to query
@@ -484,9 +486,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         pb[qs][t] = pack8<BF16>(s[qs], 8 * t);
         px[64 * (2 * qs + t)] = __builtin_bit_cast(uint4, pb[qs][t]);
       }
-    wait_but_one_step();
-    lds_barrier();   // A: P is visible to the dS waves, the next tile to every wave
-    // ---- dV^T += dO^T P (slot (g, e) of half t is row 32qs + 16t + 8(e/4) + 4g + e%4)
+    // ---- dV^T += dO^T P (slot (g, e) of half t is row 32qs + 16t + 8(e/4) + 4g + e%4): this
+    // tile's dO has been visible since the previous barrier A
     const short* tdo = qd + TILE;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
@@ -497,9 +498,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           const i16x8_t a = read_tr8(tdo + (32 * qs + 16 * t) * D, off_tr[db]);
           acc[db] = mfma32x32x16<BF16>(a, pb[qs][t], acc[db]);
         }
-    // ---- S of the next tile (past the workgroup's last step it reads a reloaded block and the
-    // result is never used)
-    compute_s(Next{});
     // scheduling: LDS reads a few ahead of their MFMAs (0x100 = LDS reads, 0x008 = MFMA)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -507,6 +505,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    wait_but_one_step();
+    lds_barrier();   // A: P is visible to the dS waves, the next tile to every wave
+    // ---- S of the next tile (past the workgroup's last step it reads a reloaded block and the
+    // result is never used)
+    compute_s(Next{});
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
