@@ -732,6 +732,12 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   // rows past the end: LSE = +inf gives P = 0
   const float lse2 = qrow < N ? Lse2[(size_t)bh * npad + qrow] : INFINITY;
   const float dd = qrow < N ? Dsum[(size_t)bh * npad + qrow] : 0.f;
+  // without a window or bias: -D of the lane's query in every register, the initial accumulator
+  // of dP^T, so that the MFMAs deliver dP - D (the first MFMA of each chain reads it and none
+  // overwrites it); the window / ALiBi variants, short of registers, add -D after the MFMAs
+  f32x16_t ddv;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ddv[r] = EXT ? 0.f : dd;
   wait_all_loads();
 
   f32x16_t acc[DB];
@@ -790,7 +796,7 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
     const short* Kb = KV(par) + 32 * kb * D;
     const short* Vb = KV(par) + TILE + 32 * kb * D;
     st = f32x16_t{};
-    dpt = f32x16_t{};
+    dpt = ddv;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const i16x8_t ak = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + off_row[kk]));
@@ -825,7 +831,7 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
           if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qrow) p = 0.f;
         }
       }
-      st[r] = p * (dpt[r] + dd);
+      st[r] = EXT ? p * (dpt[r] + dd) : p * dpt[r];
     }
     sb[0] = pack8<BF16>(st, 0);
     sb[1] = pack8<BF16>(st, 8);
