@@ -47,14 +47,20 @@ __device__ __forceinline__ float pow2_block_scale(float amax) {
   return ldexpf(1.f, e);
 }
 
+// threads per workgroup (one 128-row block): 8 waves, so that a thread holds 4 row pieces of 8
+// values at d = 128 (91 registers; with 4 waves and 8 pieces it needed 175, and two workgroups
+// per CU left the loads of a block too few waves to hide their latency)
+constexpr int kPrepThreads = 512;
+
 template <int D, bool HAD, bool POW2>
-__global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
+__global__ __launch_bounds__(kPrepThreads) void fp8_prep_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
                                                        float* __restrict__ descale, const int8_t* __restrict__ signs,
                                                        int N, int nblk, float inv_sqrt_d) {
   constexpr int LPR = D / 8;            // lanes per row
-  constexpr int RPP = 256 / LPR;        // rows per pass
+  constexpr int RPP = kPrepThreads / LPR;   // rows per pass
   constexpr int PASSES = kQBlock / RPP;
-  __shared__ float red[4];
+  constexpr int NWAVE = kPrepThreads / 64;
+  __shared__ float red[NWAVE];
   const int bh = blockIdx.x / nblk, qb = blockIdx.x % nblk;
   const int tid = threadIdx.x, sub = tid % LPR, rloc = tid / LPR;
   const int r0 = qb * kQBlock;
@@ -107,7 +113,9 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  amax = red[0];
+#pragma unroll
+  for (int i = 1; i < NWAVE; ++i) amax = fmaxf(amax, red[i]);
   const float scale = amax > 0.f ? (POW2 ? pow2_block_scale(amax) : amax / 448.f) : 1.f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -127,8 +135,8 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const float* __restrict__
 template <int D, bool HAD>
 static void launch_prep_t(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int N, int nblk, float inv,
                           bool pow2, dim3 grid, hipStream_t stream) {
-  if (pow2) hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, true>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
-  else hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, false>), grid, dim3(256), 0, stream, x, x8, descale, signs, N, nblk, inv);
+  if (pow2) hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, true>), grid, dim3(kPrepThreads), 0, stream, x, x8, descale, signs, N, nblk, inv);
+  else hipLaunchKernelGGL((fp8_prep_kernel<D, HAD, false>), grid, dim3(kPrepThreads), 0, stream, x, x8, descale, signs, N, nblk, inv);
 }
 
 hipError_t launch_fp8_prep(const float* x, uint8_t* x8, float* descale, const int8_t* signs, int B, int H, int N,
