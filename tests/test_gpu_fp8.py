@@ -183,3 +183,49 @@ def test_fp8_error_ratio_study():
           f"{r_tensor_had:.4e}, block {r_block:.4e}, block + Hadamard {r_block_had:.4e}, block + Hadamard "
           f"with power-of-two V scales (ours) {r_ours:.4e}; baseline / ours = {r_tensor / r_ours:.2f}", flush=True)
     assert r_block < r_tensor and r_ours < r_block
+
+
+def _ramp_inputs(N, kind, seed):
+    """Q, K whose scores grow along the keys by far more than the kernel's offset range: 'ramp' --
+    every query is 10 e_0 and key j is 60 (j / N) e_0, so score (i, j) = 600 j / N / sqrt(d),
+    about 76 log2 units from the first key to the last; 'jump' -- unit-normal scores with one key
+    per 128 (after the first block) lifted by 90 log2 units over its neighbours.  V is the fp8
+    workload's; the Hadamard signs are the draw's."""
+    _, _, v, signs = draw_fp8(1, 2, N, 128, seed=seed)
+    rng = np.random.default_rng(seed)
+    q = np.zeros((1, 2, N, 128), np.float32)
+    k = np.zeros((1, 2, N, 128), np.float32)
+    if kind == "ramp":
+        q[..., 0] = 10.0
+        k[..., 0] = (60.0 * np.arange(N) / N).astype(np.float32)
+    else:
+        q[:] = rng.standard_normal(q.shape).astype(np.float32)
+        k[:] = rng.standard_normal(k.shape).astype(np.float32)
+        lift = 90.0 / np.log2(np.e) * np.sqrt(128.0)        # 90 log2 units of score
+        for j in range(192, N, 128):
+            k[0, :, j] += lift * q[0, :, min(j, N - 1)] / np.maximum(
+                np.sum(q[0, :, min(j, N - 1)] ** 2, axis=-1, keepdims=True), 1e-3)
+    return q, k, v, signs
+
+
+@pytest.mark.parametrize("kind", ["ramp", "jump"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_large_maximum_growth(kind, causal):
+    """Rows whose maximum grows by more than 64 log2 units: the kernel's integer offset passes
+    its limit and the row is rebased (accumulator and row sum times 2^-k), on top of the offsets
+    applied through the MFMA scale operand.  The same per-element bound as the arithmetic test."""
+    N = 1000
+    q, k, v, signs = _ramp_inputs(N, kind, seed=1700 + N)
+    q8, qs, k8, ks, v8, vs, o, lse = _fp8_pipeline(q, k, v, signs, causal)
+    qd, kd, vd = F.dequantize(q8, qs), F.dequantize(k8, ks), F.dequantize(v8, vs)
+    ro, rlse, bound, lse_bound = _kernel_bound(qd, kd, vd, causal, 1.0 / np.sqrt(128))
+    s_c = (qd[0, 0] @ kd[0, 0].T) / np.sqrt(128) * np.log2(np.e)
+    growth = (s_c.max(axis=1) - s_c[:, :64].max(axis=1)).max()
+    assert growth > 64, f"the inputs grow the row maximum by only {growth:.1f} log2 units"
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    err = np.abs(o - ro)
+    assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
+    lerr = np.abs(lse - rlse)
+    print(f"  {kind} causal={causal}: maximum growth {growth:.1f} log2 units, O error / bound max "
+          f"{(err / bound).max():.3f}, LSE error max {lerr.max():.2e}", flush=True)
+    assert np.all(lerr <= lse_bound), f"worst LSE excess {(lerr - lse_bound).max():.3e}"
