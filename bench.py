@@ -16,7 +16,11 @@ Besides the headline value it carries:
   * errors: the GPU's outputs of the sampled K/V head groups against the oracle's (max-abs,
     tolerances, pass); the run exits non-zero when a tolerance is missed;
   * clock: the mean engine clock while the timed steps run (a probe kernel beside the same steps
-    repeated right after the timed region) and the fraction of the dense bf16 peak at that clock.
+    repeated right after the timed region) and the fraction of the dense bf16 peak at that clock;
+  * mfma_ceiling: the dense bf16 MFMA rate this machine sustains with no memory traffic at all, on
+    random N(0,1) operands (the kind of data the step multiplies) and on zero operands, each
+    with its clock, and the step's rates as fractions of the random-operand rate (the matrix
+    cores' power, and with it the clock, depends on the bits multiplied).
 """
 from __future__ import annotations
 
@@ -195,6 +199,47 @@ def clock_window(step, steps, ms_total):
     cyc = out.view(8, 2).double().cpu()
     ghz = (0.1 * cyc[:, 0] / cyc[:, 1]).tolist()
     return sum(ghz) / len(ghz), ghz
+
+
+def mfma_ceiling(dev, rates):
+    """Attainable dense bf16 MFMA rate on this machine (attn_mfma_probe: back-to-back MFMAs, two waves
+    per SIMD, no memory traffic) on random N(0,1) operands, the values the bench feeds the
+    kernels, and on zero operands; the engine clock of each (attn_clock_probe beside a second
+    run); and each named rate as a fraction of the random-operand ceiling.  The matrix cores
+    draw power according to the bits they multiply and the clock follows the power limit, so
+    the spec peak (2.4 GHz) is out of reach on random data."""
+    import torch
+
+    import exact_attention_online_amd as eao
+
+    gen = torch.Generator(device=dev).manual_seed(SEED)
+    res = {}
+    for name, data in (("random", torch.randn(1 << 23, generator=gen, device=dev).to(torch.bfloat16)),
+                       ("zero", torch.zeros(1 << 23, dtype=torch.bfloat16, device=dev))):
+        out = torch.empty(512 * 1024, dtype=torch.float32, device=dev)
+        iters = 4000                     # about 20 ms per launch
+        eao.mfma_probe(data, out, iters)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(eao.mfma_probe(data, out, iters) for _ in range(3))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        clk = torch.zeros(16, dtype=torch.int64, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        torch.cuda.synchronize()
+        eao.clock_probe(clk, max(1, int(ms * 1e5)), stream=side)
+        for _ in range(3):
+            eao.mfma_probe(data, out, iters)
+        torch.cuda.synchronize()
+        cyc = clk.view(8, 2).double().cpu()
+        res[name] = (flops / (ms * 1e-3) / 1e12, float((0.1 * cyc[:, 0] / cyc[:, 1]).mean()))
+    return {"random_operands_tflops": round(res["random"][0], 1), "random_operands_clock_ghz": round(res["random"][1], 3),
+            "zero_operands_tflops": round(res["zero"][0], 1), "zero_operands_clock_ghz": round(res["zero"][1], 3),
+            "frac_of_random_ceiling": {k: round(v / res["random"][0], 4) for k, v in rates.items()},
+            "source": "attn_mfma_probe: 1024 workgroups x 8 waves x 32 x 4000 v_mfma_f32_32x32x16_bf16 on 2^23 "
+                      "operand values, 3 launches timed with events"}
 
 
 def clock_record(ghz, per_xcd, rates):
@@ -823,6 +868,8 @@ def main():
     }
     out["clock"] = clock_record(clk_ghz, clk_xcd, {"fwd+bwd": value, "fwd": f_fwd / (fwd_ms * 1e-3) / 1e12,
                                                     "bwd_dkdv": dkdv_tflops})
+    out["mfma_ceiling"] = mfma_ceiling(dev, {"fwd+bwd": value, "fwd": f_fwd / (fwd_ms * 1e-3) / 1e12,
+                                             "bwd_dkdv": dkdv_tflops})
     failed = False
     if not args.no_cpu_baseline:
         out["cpu_baseline"], outs = cpu_baseline(w, qc, kc, vc, doc, args.cpu_seconds)

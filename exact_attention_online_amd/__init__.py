@@ -12,13 +12,13 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "fwd_splitkv_noalloc", "splitkv_workspace_size", "attention", "clock_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
+    "fwd_splitkv", "fwd_splitkv_noalloc", "splitkv_workspace_size", "attention", "clock_probe", "mfma_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
 ]
 
 F16, BF16, FP8_E4M3, F32 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
-           "attn_fwd_splitkv_noalloc", "attn_clock_probe", "attn_status_string")
+           "attn_fwd_splitkv_noalloc", "attn_clock_probe", "attn_mfma_probe", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -74,6 +74,8 @@ def load():
     lib.attn_fp8_prep.restype = i
     lib.attn_clock_probe.argtypes = [vp, i, ctypes.c_longlong, vp]
     lib.attn_clock_probe.restype = i
+    lib.attn_mfma_probe.argtypes = [vp, ctypes.c_longlong, vp, i, i, vp]
+    lib.attn_mfma_probe.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -477,6 +479,21 @@ def clock_probe(out, ticks: int, stream=None):
     st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
     _check(load().attn_clock_probe(_ptr(out), out.numel() // 2, int(ticks), ctypes.c_void_p(st)))
     return out
+
+
+def mfma_probe(data, out, iters: int, stream=None):
+    """Launch attn_mfma_probe: data is a contiguous bf16 device tensor (the operand bits, at
+    least 8192 values, a multiple of 8), out a float32 device tensor of 512 * groups entries;
+    runs on `stream` (default: the current stream).  Returns the launch's flop count."""
+    torch = _torch()
+    if data.dtype != torch.bfloat16 or not data.is_cuda or not data.is_contiguous():
+        raise AttnError("data must be a contiguous bf16 device tensor")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.numel() % 512:
+        raise AttnError("out must be a contiguous float32 device tensor of 512 * groups entries")
+    groups = out.numel() // 512
+    st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
+    _check(load().attn_mfma_probe(_ptr(data), data.numel(), _ptr(out), groups, int(iters), ctypes.c_void_p(st)))
+    return groups * 8 * 32 * int(iters) * 32768
 
 
 _AttentionFn = None

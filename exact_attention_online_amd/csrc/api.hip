@@ -46,6 +46,7 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               void* workspace, hipStream_t stream);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 hipError_t launch_clock_probe(unsigned long long* out, int groups, long long ticks, hipStream_t stream);
+hipError_t launch_mfma_probe(const uint16_t* data, size_t n, float* out, int groups, int iters, hipStream_t stream);
 size_t splitkv_scratch_bytes();
 hipError_t splitkv_scratch_address(void** out);
 }  // namespace eao
@@ -328,6 +329,13 @@ int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_
   if (out == nullptr || ((uintptr_t)out & 15u) != 0) return ATTN_ERR_INVALID;
   if (groups < 1 || groups > 1024 || ticks < 1 || ticks > 1000000000LL) return ATTN_ERR_INVALID;
   return eao::launch_clock_probe(out, groups, ticks, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, attn_stream_t stream) {
+  if (!aligned16(data) || !aligned16(out)) return ATTN_ERR_INVALID;
+  if (n < 8192 || n % 8 != 0 || groups < 1 || groups > 65536 || iters < 1 || iters > (1 << 20)) return ATTN_ERR_INVALID;
+  const hipError_t e = eao::launch_mfma_probe((const uint16_t*)data, (size_t)n, out, groups, iters, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* signs, int B, int H, int N, int d,

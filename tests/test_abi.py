@@ -223,6 +223,19 @@ def test_clock_probe_rejects_bad_arguments():
     assert lib.attn_clock_probe(P, 8, 10 ** 9 + 1, NULL) == 1
 
 
+def test_mfma_probe_rejects_bad_arguments():
+    lib = eao.load()
+    assert lib.attn_mfma_probe(NULL, 8192, P, 1, 1, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, NULL, 1, 1, NULL) == 1
+    assert lib.attn_mfma_probe(ctypes.c_void_p(0x7F0000001008), 8192, P, 1, 1, NULL) == 1   # misaligned
+    assert lib.attn_mfma_probe(P, 8184, P, 1, 1, NULL) == 1          # fewer than 8192 values
+    assert lib.attn_mfma_probe(P, 8196, P, 1, 1, NULL) == 1          # not a multiple of 8
+    assert lib.attn_mfma_probe(P, 8192, P, 0, 1, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 65537, 1, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 1, 0, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 1, (1 << 20) + 1, NULL) == 1
+
+
 def test_splitkv_noalloc_rejects_on_the_host():
     """The allocation-free split-KV entry point checks its arguments, and that the problem's
     partials fit its static scratch, before any HIP call (so without a GPU too)."""
