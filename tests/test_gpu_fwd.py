@@ -148,12 +148,18 @@ def _ramp_inputs(kind, N, d, dtype, seed):
     """Q rows and K rows along one direction u with key weights that ramp up ('up': the running
     maximum grows by far more than 2^8 from tile to tile, so the rescale of the accumulator runs
     on every tile), ramp down ('down': the first tile holds the maximum) or stay small but for one
-    late key ('spike': one jump).  Scores reach about 100 (natural units)."""
+    late key ('spike': one jump).  Scores reach about 100 (natural units).  'stairs' raises the
+    level by about 6 log2 units per 64-key tile and 'plateau' once, after the first tile: a lane's
+    32 keys of such a tile then sum to far more than 2^8 against the running maximum while the
+    maximum itself grows by less than 2^8, so the d = 128 kernels rescale on the row-sum test
+    alone (and recompute the tile's probabilities)."""
     g = np.random.Generator(np.random.PCG64(seed))
     u = g.standard_normal(d)
     u /= np.linalg.norm(u)
     t = np.arange(N) / max(N - 1, 1)
-    alpha = {"up": 38.0 * t, "down": 38.0 * (1.0 - t), "spike": np.where(np.arange(N) == (7 * N) // 8, 38.0, 1.0)}[kind]
+    step = 6.0 / (30.0 / np.sqrt(d) * np.log2(np.e))     # key weight of 6 log2 units of score
+    alpha = {"up": 38.0 * t, "down": 38.0 * (1.0 - t), "spike": np.where(np.arange(N) == (7 * N) // 8, 38.0, 1.0),
+             "stairs": step * (np.arange(N) // 64), "plateau": step * (np.arange(N) >= 64)}[kind]
     q = (30.0 * u)[None, :] + 0.3 * g.standard_normal((N, d))
     k = alpha[:, None] * u[None, :] + 0.3 * g.standard_normal((N, d))
     v = g.standard_normal((N, d))
@@ -161,7 +167,7 @@ def _ramp_inputs(kind, N, d, dtype, seed):
     return tuple(round_to(x.reshape(shape).astype(np.float32), dtype) for x in (q, k, v))
 
 
-@pytest.mark.parametrize("kind", ["up", "down", "spike"])
+@pytest.mark.parametrize("kind", ["up", "down", "spike", "stairs", "plateau"])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_running_maximum_growth(kind, dtype, causal):
