@@ -181,22 +181,24 @@ def test_forward_running_maximum_growth(kind, dtype, causal):
 
 
 # ---------------------------------------------------------------- block size chosen by grid size
-# 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512, else 128-row blocks (4 waves).  Below:
-# 2*64*ceil(1100/256) = 640 blocks, so the 8-wave path, over every output with a ragged tail
-# (1100 = 4*256 + 76); one head alone (1*1*5 blocks) takes the 4-wave path, and each row's
-# arithmetic is the same in both, so the two agree bit for bit.
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+# 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512 and, for d = 128, the rows are not short
+# (N > 2048, and N > 4096 when causal); else 128-row blocks (4 waves).  Below: 1*32*ceil(4200/256)
+# = 544 blocks at d = 128 (N = 4200 = 16*256 + 104) and 2*64*ceil(1100/256) = 640 at d = 64, so
+# the 8-wave path, over every output with a ragged tail; one head alone takes the 4-wave path,
+# and each row's arithmetic is the same in both, so the two agree bit for bit.
+@pytest.mark.parametrize("dtype,d,B,Hq,Hkv,N,heads", [("bf16", 128, 1, 32, 8, 4200, ((0, 0), (0, 17), (0, 31))),
+                                                     ("fp16", 64, 2, 64, 16, 1100, ((0, 0), (1, 37), (1, 63)))])
 @pytest.mark.parametrize("causal", [False, True])
-def test_large_grid_full_and_block_size_invariance(dtype, d, causal):
-    B, Hq, Hkv, N = 2, 64, 16, 1100
+def test_large_grid_full_and_block_size_invariance(dtype, d, B, Hq, Hkv, N, heads, causal):
     assert B * Hq * ((N + 255) // 256) >= 512
+    assert not (d == 128 and (N <= 2048 or (causal and N <= 4096)))
     q, k, v = _inputs(B, Hq, Hkv, N, d, dtype, seed=20 + d + causal)
     o, lse = _run(q, k, v, causal)
     ro, rlse = A.forward(q, k, v, causal, 1.0 / np.sqrt(d))
     assert np.abs(f64(o) - ro).max() <= TOL_O[dtype]
     assert np.abs(f64(lse) - rlse).max() <= TOL_LSE
     G = Hq // Hkv
-    for b, h in ((0, 0), (1, 37), (1, 63)):
+    for b, h in heads:
         g = h // G
         o1, l1 = _run(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], causal)
         assert torch.equal(o1[0, 0].cpu(), o[b, h].cpu()), (b, h)
