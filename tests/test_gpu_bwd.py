@@ -184,10 +184,12 @@ def test_backward_running_maximum_growth(kind, dtype, causal):
 
 
 # ---------------------------------------------------------------- dQ block size chosen by grid size
-# The dQ kernel takes 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512, else 128-row blocks
-# (4 waves).  Below: 4*64*ceil(300/256) = 512 blocks, so the 8-wave path, over every output with a
-# ragged tail (300 = 256 + 44), four query heads per K/V head; one head alone takes the 4-wave
-# path, and a row's arithmetic is the same in both, so its dQ agrees bit for bit.  Summed over four
+# The dQ kernel takes 256-row blocks (8 waves) when B*Hq*ceil(N/256) >= 512 and, at d = 128, the
+# rows are not short (N > 2048, and N > 4096 when causal), else 128-row blocks (4 waves).  Below:
+# 4*64*ceil(300/256) = 512 blocks, four query heads per K/V head, over every output with a ragged
+# tail (300 = 256 + 44): the 8-wave path at d = 64, the 4-wave path at d = 128 (short rows; the
+# next test covers its 8-wave path); one head alone takes the 4-wave path, and a row's
+# arithmetic is the same in both, so its dQ agrees bit for bit.  Summed over four
 # query heads dV reaches |11| here, where half a bf16 step is 2^-5 > 3e-2: float32 gradients are
 # held to the bar, bf16 gradients to the bar plus their own rounding.
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
@@ -210,6 +212,27 @@ def test_backward_large_grid_full_and_block_size_invariance(dtype, d, causal):
         dq1, _, _ = _gpu_grads(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
                                do[b:b + 1, h:h + 1], causal)
         assert torch.equal(dq1[0, 0].cpu(), dq16[b, h].cpu()), (b, h)
+
+
+# The 8-wave dQ path at d = 128: B=1, Hq=32, Hkv=8, N=4200 (1*32*17 = 544 blocks, rows past the
+# short-row limits, ragged tail 4200 = 16*256 + 104).  dQ of three heads agrees bit for bit with
+# one-head launches (4-wave path); the first K/V group (its four query heads) against the oracle.
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_dq_long_rows_block_size_invariance(causal):
+    B, Hq, Hkv, N, d = 1, 32, 8, 4200, 128
+    assert B * Hq * ((N + 255) // 256) >= 512 and N > 4096
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, "bf16", seed=95 + causal)
+    dq, dk, dv = _gpu_grads(q, k, v, do, causal, grad_dtype=torch.float32)
+    G = Hq // Hkv
+    for h in (0, 17, 31):
+        g = h // G
+        dq1, _, _ = _gpu_grads(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], do[:, h:h + 1], causal,
+                               grad_dtype=torch.float32)
+        assert torch.equal(dq1[0, 0].cpu(), dq[0, h].cpu()), h
+    rq, rk, rv = A.backward(q[:, 0:G], k[:, 0:1], v[:, 0:1], do[:, 0:G], causal, 1.0 / np.sqrt(d))
+    assert _err(dq[:, 0:G], rq) <= TOL["bf16"]
+    assert _err(dk[:, 0:1], rk) <= TOL["bf16"]
+    assert _err(dv[:, 0:1], rv) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
