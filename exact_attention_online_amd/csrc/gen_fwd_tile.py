@@ -224,8 +224,9 @@ def check(lines):
     """Static checks of one block: the LDS read feeding each MFMA (the K or V^T fragment its
     operands name) has completed and not been overwritten (s_waitcnt lgkmcnt; LDS operations
     complete in order), exp results are not read by the next instruction, lgkmcnt stays within
-    its field, nothing is left in flight, and the block ends TAIL wait states after its last
-    MFMA.  Raises AssertionError on a violation."""
+    its field, nothing is left in flight, the first MFMA comes two wait states after the block
+    starts (its operands may have been written by vector code just before) and the block ends
+    TAIL wait states after its last MFMA.  Raises AssertionError on a violation."""
     pending = []            # (register, source) of LDS reads not yet known complete, oldest first
     done = {}               # register -> source of the completed read it holds
     for i, ins in enumerate(lines):
@@ -261,6 +262,10 @@ def check(lines):
                     got = done.get(reg)
                     assert got is not None and got[0] == f"%[va{2 * db + h}]" and \
                         got[1] % TILE_BYTES == (32 * kb + 16 * t) * D * 2, f"V^T fragment of {ins} not ready"
+    # a packed P^T operand written by vector code before the block is two instructions old at
+    # the first MFMA at the latest
+    first = min(i for i, x in enumerate(lines) if x.startswith("v_mfma"))
+    assert sum(_wait_states(x) for x in lines[:first]) >= 2, "first MFMA too close to the block start"
     last = max(i for i, x in enumerate(lines) if x.startswith("v_mfma"))
     assert sum(_wait_states(x) for x in lines[last + 1:]) >= TAIL, "short tail after the last MFMA"
     assert not pending, "LDS reads left in flight at the end of the block"
