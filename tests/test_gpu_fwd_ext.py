@@ -34,7 +34,8 @@ def _run(q, k, v, causal, window, slopes):
     return f64(o), f64(lse)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+# fp16 at d = 128 runs the hand-scheduled fp16 tile step under the window masks (without ALiBi)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64), ("fp16", 128)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,window", [(1, 1), (63, 16), (200, 1), (200, 64), (515, 100), (515, 128), (300, 1000)])
 @pytest.mark.parametrize("alibi", [False, True])
@@ -44,7 +45,10 @@ def test_fwd_ext_small_full(dtype, d, causal, N, window, alibi):
     sl = _slopes(Hq) if alibi else None
     o, lse = _run(q, k, v, causal, window, sl)
     ro, rlse = VA.forward(q, k, v, causal, 1.0 / np.sqrt(d), window=window, slopes=sl)
-    assert np.abs(o - ro).max() <= TOL_O[dtype]
+    # a small window with ALiBi concentrates a row on a few keys, so O reaches several times its
+    # unit-normal size: the bar is the unit-normal one relative to max(1, max |O|), as the output's
+    # own rounding and that of the probabilities scale with |O|
+    assert np.abs(o - ro).max() <= TOL_O[dtype] * max(1.0, np.abs(ro).max())
     assert np.abs(lse - rlse).max() <= TOL_LSE
 
 
