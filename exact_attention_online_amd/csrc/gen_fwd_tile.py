@@ -38,7 +38,8 @@ DB = D // 32            # 32-row blocks of O^T
 TILE_BYTES = 64 * D * 2  # one 64-key tile of 16-bit K or V in LDS
 R = 4                   # LDS operand reads in flight ahead of their MFMA
 NP = 12                 # probability temporaries
-TAIL = 20               # wait states after a block's last MFMA
+TAIL = 12               # wait states after a block's last MFMA (the distance the compiler
+                        # keeps between a 32x32x16 MFMA and a vector read of its result)
 RING = 256 - 4 * R      # first register of the operand ring
 PT = RING - NP          # first probability temporary
 # issue-cycle weights used to spread the vector work over the MFMA slots
