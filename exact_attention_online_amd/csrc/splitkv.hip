@@ -10,15 +10,17 @@
 //   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
 //
 // gfx950 mapping
-//   * split kernel: one workgroup of 4 waves per (batch, K/V head, split, group of 32 rows).
+//   * split kernel: one workgroup of one wave per (batch, K/V head, split, group of 32 rows).
 //     The query rows that use the K/V head -- G = Hq / Hkv heads times Nq rows -- are taken 32 at
 //     a time as the 32 columns of one MFMA tile (transposed formulation as in the main forward:
 //     a lane owns one row); the workgroups of one split's row groups are adjacent in the grid,
-//     so beyond the first they find the split's keys in L2.  Key
-//     tiles of 128 go straight from HBM into double-buffered LDS (direct buffer -> LDS loads);
-//     each wave takes its own 32 keys of every tile and keeps its own running max, sum and
-//     O^T, so the four waves stream disjoint keys and are merged once, through LDS, at the end.
-//     The kernel is bound by HBM bandwidth (every key is read once per K/V head).
+//     so beyond the first they find the split's keys in L2.  The wave streams its split's keys
+//     in stages of 32 (one MFMA tile of keys) through a ring of four LDS slots filled by direct
+//     buffer -> LDS loads issued three stages ahead, and waits only for the oldest stage (a
+//     counter wait; the wave is alone in its workgroup, so there is no barrier): two to three
+//     stages, 32-48 KB at d = 128, stay in flight per wave.  The kernel is bound by HBM
+//     bandwidth (every key is read once per K/V head); a double-buffered tile shared by four
+//     waves left at most one tile in flight, which drained before each new request.
 //   * merge kernel: one wave per output row.
 //
 // Causal alignment for Nq < Nk (bottom-right): query i sits at position Nk - Nq + i and sees
@@ -30,7 +32,17 @@
 
 namespace eao {
 
-constexpr int kSkTile = 128;   // keys per tile (32 per wave)
+constexpr int kSkTile = 128;   // split granularity: every split but the last holds a multiple of 128 keys
+constexpr int kSkStage = 32;   // keys per pipeline stage
+constexpr int kSkSlots = 4;    // LDS ring slots (stages) per wave
+
+// Wait until at most n of this wave's vector-memory operations are outstanding and its LDS
+// operations have completed (vmcnt is six bits on gfx9: bits 3:0 and 15:14; expcnt left at 7).
+template <int n>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
+}
 
 // Static scratch of the allocation-free entry point: the split partials (float O and LSE of
 // every split) live here instead of in a caller's workspace.  Each GPU holds its own copy for
@@ -75,11 +87,12 @@ void splitkv_plan(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits, int* s
   const int tiles = (Nk + kSkTile - 1) / kSkTile;
   int s = num_splits;
   if (s <= 0) {
-    // about two workgroups per compute unit, but splits of at least 8 tiles: shorter splits
-    // spend more time in their prologue and the merge than they save
+    // about two workgroups (waves) per compute unit -- as many as the LDS of one CU holds at
+    // d = 128 -- but splits of at least 4 x 128 keys: shorter splits spend more time in their
+    // first load and the merge than they save
     const int wg = B * Hkv * splitkv_row_groups(Hq, Hkv, Nq);
     const int want = (2 * 256 + wg - 1) / wg;
-    s = want < tiles / 8 ? want : tiles / 8;
+    s = want < tiles / 4 ? want : tiles / 4;
   }
   s = s < 1 ? 1 : (s > tiles ? tiles : s);
   const int tps = (tiles + s - 1) / s;                     // tiles per split
@@ -95,36 +108,40 @@ size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, in
 }
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __restrict__ Q,
-                                                           const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V, float* __restrict__ Opart,
-                                                           float* __restrict__ Lpart, int B, int Hq, int Hkv, int Nq,
-                                                           int Nk, int S, int L, float c /* scale * log2(e) */) {
+__global__ __launch_bounds__(64) void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                      const uint16_t* __restrict__ V, float* __restrict__ Opart,
+                                                      float* __restrict__ Lpart, int B, int Hq, int Hkv, int Nq, int Nk,
+                                                      int S, int L, float c /* scale * log2(e) */) {
   constexpr int CH = D / 8, KK = D / 16, DB = D / 32;
-  constexpr int TILE = kSkTile * D;                 // 16-bit elements per K or V tile
-  constexpr int PIECES = TILE * 2 / 1024;           // 1 KB direct-load pieces per tile
-  static_assert(PIECES % 4 == 0, "each wave moves the same number of pieces");
-  __shared__ __attribute__((aligned(1024))) short k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) short k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) short v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) short v_lds1[TILE];
-  __shared__ float red_m[4][32], red_l[4][32];
-  auto Ks = [&](auto par) -> short* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
+  constexpr int STAGE = kSkStage * D;               // 16-bit elements of K (or V) per stage
+  constexpr int PIECES = STAGE * 2 / 1024;          // 1 KB direct loads per tensor and stage
+  constexpr int LPS = 2 * PIECES;                   // loads per stage (K and V)
+  static_assert(PIECES * 64 * 8 == STAGE, "a stage is whole 1 KB pieces");
+  static_assert(2 * LPS < 64, "two stages' loads fit the counter");
+  // four slots [K | V], distinct objects so that the compiler tracks each slot's loads apart
+  __shared__ __attribute__((aligned(1024))) short kv0[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) short kv1[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) short kv2[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) short kv3[2 * STAGE];
+  auto slot = [&](auto sl) __attribute__((always_inline)) -> short* {
+    constexpr int SL = decltype(sl)::value;
+    if constexpr (SL == 0) return kv0;
+    else if constexpr (SL == 1) return kv1;
+    else if constexpr (SL == 2) return kv2;
+    else return kv3;
   };
-  auto Vs = [&](auto par) -> short* __attribute__((always_inline)) {
-    if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
-  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int G16 = lane >> 4, li = lane & 15;
+  const int lane = threadIdx.x;
+  const int g = lane >> 5, l32 = lane & 31;
   const int G = Hq / Hkv, R = G * Nq, RG = (R + 31) / 32;
   const int rg = blockIdx.x % RG, s = (blockIdx.x / RG) % S, bkv = blockIdx.x / (RG * S);
   const int b = bkv / Hkv, kvh = bkv % Hkv;
-  const int r0 = 32 * rg;                           // first row of this workgroup's group
   // this lane's query row: head kvh * G + row / Nq, row row % Nq (rows >= R are padding)
-  const int row = r0 + l32;
+  const int row = 32 * rg + l32;
   const bool row_ok = row < R;
   const int gh = row_ok ? row / Nq : 0, qi = row_ok ? row % Nq : 0;
   const int hq = kvh * G + gh;
@@ -141,60 +158,63 @@ __global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __res
 
   const int ks = s * L;
   const int ke = min(Nk, ks + L);
-  const int ntiles = (ke - ks + kSkTile - 1) / kSkTile;
+  const int nst = (ke - ks + kSkStage - 1) / kSkStage;
   const size_t kv_off = (size_t)bkv * Nk * D;
   const uint32_t head_bytes = (uint32_t)Nk * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
-  uint32_t goff[PIECES / 4];
+  // lane's byte offset within a stage for piece i: LDS chunk (r, c) holds logical chunk c ^ swz(r)
+  uint32_t goff[PIECES];
 #pragma unroll
-  for (int i = 0; i < PIECES / 4; ++i) {
-    const int p = 64 * (4 * i + w) + lane;
+  for (int i = 0; i < PIECES; ++i) {
+    const int p = 64 * i + lane;
     const int r = p / CH, pch = p % CH;
     goff[i] = ((uint32_t)r * D + ((pch ^ swz<D>(r)) << 3)) * 2;
   }
-  auto load_tile = [&](int j, auto par) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)(ks + j * kSkTile) * D * 2;
-    short* kd = Ks(par);
-    short* vd = Vs(par);
+  auto load_stage = [&](int j, auto sl) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(ks + j * kSkStage) * D * 2;
+    short* kd = slot(sl);
 #pragma unroll
-    for (int i = 0; i < PIECES / 4; ++i) {
-      buffer_load16_lds(krs, kd + 512 * (4 * i + w), goff[i] + base);
-      buffer_load16_lds(vrs, vd + 512 * (4 * i + w), goff[i] + base);
+    for (int i = 0; i < PIECES; ++i) {
+      buffer_load16_lds(krs, kd + 512 * i, goff[i], base);
+      buffer_load16_lds(vrs, kd + STAGE + 512 * i, goff[i], base);
     }
   };
   int off_k[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) off_k[kk] = (32 * w) * D + chunk_index<D>(l32, 2 * kk + g) * 8;
+  for (int kk = 0; kk < KK; ++kk) off_k[kk] = chunk_index<D>(l32, 2 * kk + g) * 8;
   int off_v[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      off_v[db][hh] = (32 * w) * D +
-                      elem_index<D>(4 * (G16 >> 1) + (li >> 2) + 8 * hh, 32 * db + 16 * (G16 & 1) + 4 * (li & 3));
+    for (int hh = 0; hh < 2; ++hh) off_v[db][hh] = tr_off<D>(lane, db, hh);
 
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   float m = -INFINITY, l = 0.f;
 
-  // tiles that may hold keys a row cannot see (past Nk, or after its causal position)
-  const int limit = CAUSAL ? Nk - Nq + 1 : Nk;      // keys below this are visible to every row
-  auto tile = [&](int j, auto par, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    using Other = std::integral_constant<int, 1 - decltype(par)::value>;
-    if (j + 1 < ntiles) load_tile(j + 1, Other{});
-    const short* Kb = Ks(par);
-    const short* Vb = Vs(par);
+  // keys below klim are visible to every row (none past Nk, none after a row's causal position)
+  const int klim = min(ke, CAUSAL ? Nk - Nq + 1 : Nk);
+  auto stage = [&](int j, auto sl) __attribute__((always_inline)) {
+    constexpr int SL = decltype(sl)::value;
+    // stages j .. j + ahead are in flight, j the oldest: wait for it (and for the LDS reads of
+    // stage j - 1, whose slot the next request overwrites)
+    const int ahead = min(kSkSlots - 2, nst - 1 - j);
+    if (ahead >= 2) wait_vmem_lds<2 * LPS>();
+    else if (ahead == 1) wait_vmem_lds<LPS>();
+    else wait_vmem_lds<0>();
+    if (j + kSkSlots - 1 < nst) load_stage(j + kSkSlots - 1, std::integral_constant<int, (SL + kSkSlots - 1) % kSkSlots>{});
+    const short* Kb = slot(sl);
+    const short* Vb = Kb + STAGE;
     f32x16_t st = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const i16x8_t a = __builtin_bit_cast(i16x8_t, *(const uint4*)(Kb + off_k[kk]));
       st = mfma32x32x16<BF16>(a, qf[kk], st);
     }
-    const int kw0 = ks + j * kSkTile + 32 * w;      // this wave's first key
-    if constexpr (MASK) {
+    const int kw0 = ks + j * kSkStage;
+    if (kw0 + kSkStage > klim) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -216,91 +236,67 @@ __global__ __launch_bounds__(256, 1) void fwd_split_kernel(const uint16_t* __res
     }
     m = mt;
     l = l * alpha + rs;
+    // the accumulator changes only where a row's maximum grew (alpha = 1 leaves it as it is)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
     const i16x8_t pf[2] = {pack8<BF16>(st, 0), pack8<BF16>(st, 8)};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const i16x4_t lo = ds_read_tr16(Vb + 16 * t * D + off_v[db][0]);
-        const i16x4_t hi = ds_read_tr16(Vb + 16 * t * D + off_v[db][1]);
-        const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = mfma32x32x16<BF16>(a, pf[t], o[db]);
-      }
-    wait_all_loads();
-    __syncthreads();
+      for (int db = 0; db < DB; ++db) o[db] = mfma32x32x16<BF16>(read_tr8(Vb + 16 * t * D, off_v[db]), pf[t], o[db]);
   };
 
-  if (ntiles > 0) load_tile(0, Par0{});
-  wait_all_loads();
-  __syncthreads();
-  // tiles [0, jmask) lie wholly below `limit`
-  const int jmask = min(ntiles, max(0, (limit - ks) / kSkTile));
-  int j = 0;
-  for (; j + 1 < jmask; j += 2) {
-    tile(j, Par0{}, std::false_type{});
-    tile(j + 1, Par1{}, std::false_type{});
-  }
-  if (j < jmask) {
-    tile(j, Par0{}, std::false_type{});
-    ++j;
-  }
-  for (; j < ntiles; ++j) {
-    if (j & 1) tile(j, Par1{}, std::true_type{});
-    else tile(j, Par0{}, std::true_type{});
+  if (nst > 0) load_stage(0, S0{});
+  if (nst > 1) load_stage(1, S1{});
+  if (nst > 2) load_stage(2, S2{});
+  for (int j = 0; j < nst; j += kSkSlots) {
+    stage(j, S0{});
+    if (j + 1 >= nst) break;
+    stage(j + 1, S1{});
+    if (j + 2 >= nst) break;
+    stage(j + 2, S2{});
+    if (j + 3 >= nst) break;
+    stage(j + 3, S3{});
   }
 
-  // merge the four waves (disjoint keys, same rows): M = max m_w, L = sum l_w 2^(m_w - M),
-  // O = sum O_w 2^(m_w - M) / L; the K/V buffers are free now and hold the four O^T
+  // the two halves of the wave hold different keys of the same rows and the same maximum
   const float lt = sum_halves(l);
-  if (g == 0) {
-    red_m[w][l32] = m;
-    red_l[w][l32] = lt;
-  }
-  __syncthreads();
-  float mall = -INFINITY;
+  if (row_ok) {
+    const size_t prow = (size_t)s * B * Hq * Nq + ((size_t)b * Hq + hq) * Nq + qi;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* op = Opart + prow * D;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) mall = fmaxf(mall, red_m[ww][l32]);
-  const float fw = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mall);
-  // [2 waves][32 rows][D] fp32 fills one K (waves 0, 1) or V (waves 2, 3) buffer exactly
-  static_assert(2 * 32 * D * 4 == TILE * 2, "two waves' O^T fill one tile buffer");
-  float* ost_k = (float*)k_lds0;
-  float* ost_v = (float*)v_lds0;
-  float* ost = (w < 2 ? ost_k : ost_v) + (w & 1) * 32 * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
-      ost[l32 * D + d] = o[db][r] * fw;
-    }
-  __syncthreads();
-  // 256 threads x (32 rows x D) / 256 outputs each; rows >= R are not written
-  const size_t prow0 = (size_t)s * B * Hq * Nq;      // partial rows of split s
-  for (int e = tid; e < 32 * D; e += 256) {
-    const int rr = e / D, d = e % D;
-    if (r0 + rr >= R) continue;
-    float mtot = -INFINITY, ltot = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mtot = fmaxf(mtot, red_m[ww][rr]);
-    float sum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float mw = red_m[ww][rr];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mtot);
-      ltot += red_l[ww][rr] * f;
-      sum += (ww < 2 ? ost_k : ost_v)[((ww & 1) * 32 + rr) * D + d];
-    }
-    const int ghh = (r0 + rr) / Nq, qq = (r0 + rr) % Nq;
-    const size_t prow = prow0 + ((size_t)b * Hq + kvh * G + ghh) * Nq + qq;
-    Opart[prow * D + d] = ltot > 0.f ? sum / ltot : 0.f;
-    if (d == 0) Lpart[prow] = ltot > 0.f ? (mtot + __log2f(ltot)) * kLn2 : -INFINITY;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 val = {o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                            o[db][4 * q4 + 3] * inv};
+        *(float4*)(op + 32 * db + 8 * q4 + 4 * g) = val;
+      }
+    if (g == 0) Lpart[prow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
-// One wave per output row: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s; lane l
-// handles elements 2l and 2l + 1 (lanes >= D / 2 only join the LSE).
+// Sum and maximum over the 64 lanes of a wave (a fixed butterfly order: every lane gets the same
+// value, and the result does not depend on the launch).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per output row: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  The lanes
+// read the splits' logsumexps 64 at a time (lane i holds split c + i of a chunk and its weight);
+// lane l then accumulates elements 2l and 2l + 1 over the splits in order, each split's weight
+// broadcast from the lane that holds it, the loads of 16 splits in flight together (lanes >=
+// D / 2 only take part in the logsumexp).
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __restrict__ Opart,
                                                               const float* __restrict__ Lpart, uint16_t* __restrict__ O,
@@ -308,20 +304,39 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
+  // the first 64 logsumexps are loaded once, for the maximum and for the weights
+  const float ls0 = lane < S ? Lpart[(size_t)lane * rows + row] : -INFINITY;
+  float mx = ls0;
+  for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
+  mx = wave_max(mx);
   const bool act = lane < D / 2;
-  float a0 = 0.f, a1 = 0.f, wsum = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = Lpart[(size_t)s * rows + row];
+  float a0 = 0.f, a1 = 0.f, wpart = 0.f;
+  auto weight = [](float w, int i) __attribute__((always_inline)) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+  };
+  for (int c = 0; c < S; c += 64) {
+    const float ls = c == 0 ? ls0 : (c + lane < S ? Lpart[(size_t)(c + lane) * rows + row] : -INFINITY);
     const float wgt = (ls == -INFINITY) ? 0.f : __expf(ls - mx);
-    wsum += wgt;
-    if (act) {
-      const float2 ov = *(const float2*)(Opart + ((size_t)s * rows + row) * D + 2 * lane);
-      a0 += wgt * ov.x;
-      a1 += wgt * ov.y;
+    wpart += wgt;
+    const int n = min(64, S - c);
+    const float* op = Opart + ((size_t)c * rows + row) * D + 2 * lane;
+    const size_t step = (size_t)rows * D;           // floats from one split's row to the next's
+    // batches of 16 splits with their loads in flight together; past the chunk's last split the
+    // index stays on that split and the weight (held by a lane past S) is zero
+    for (int i = 0; i < n; i += 16) {
+      float2 ov[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        ov[u] = act ? *(const float2*)(op + (size_t)min(i + u, n - 1) * step) : float2{0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float w = weight(wgt, i + u);
+        a0 += w * ov[u].x;
+        a1 += w * ov[u].y;
+      }
     }
   }
+  const float wsum = wave_sum(wpart);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if (act) *(uint32_t*)(O + (size_t)row * D + 2 * lane) = pack2<BF16>(a0 * inv, a1 * inv);
   if (lane == 0) LSE[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
@@ -337,7 +352,7 @@ static hipError_t launch_split_t(const void* q, const void* k, const void* v, vo
   const int RG = splitkv_row_groups(Hq, Hkv, Nq);
   float* opart = (float*)workspace;
   float* lpart = (float*)((char*)workspace + ((size_t)S * rows * D * 4 + 255) / 256 * 256);
-  hipLaunchKernelGGL((fwd_split_kernel<BF16, D, CAUSAL>), dim3((unsigned)(B * Hkv * S * RG)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_split_kernel<BF16, D, CAUSAL>), dim3((unsigned)(B * Hkv * S * RG)), dim3(64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, opart, lpart, B, Hq, Hkv, Nq, Nk,
                      S, L, scale * kLog2e);
   hipError_t e = hipGetLastError();

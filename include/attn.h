@@ -208,7 +208,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
  *   causal: query i sits at position Nk - Nq + i and sees keys j <= Nk - Nq + i (with Nq = 1
  *   every key is visible).
  *   num_splits: splits per (batch, K/V head), 0 = chosen for about two workgroups per compute
- *   unit with splits of at least 1024 keys; clamped to the number of 128-key tiles.
+ *   unit with splits of at least 512 keys; clamped to the number of 128-key tiles.
  *   workspace: device memory of at least attn_fwd_splitkv_workspace_size() bytes (the float
  *   partial outputs and logsumexps of every split), 256-byte aligned, owned by the caller.
  * Returns an attn_status_t. */
