@@ -50,6 +50,9 @@ CASES = [
     (1, 8, 8, 33, 1000, 64, "fp16", False, 2),
     (1, 40, 1, 1, 4096, 128, "bf16", False, 0),
     (1, 2, 1, 100, 100, 128, "fp16", True, 1),
+    # more than 64 splits: the merge takes the logsumexps in chunks of 64 lanes, the last ragged
+    (1, 8, 2, 2, 16700, 128, "bf16", True, 131),
+    (1, 4, 1, 3, 9000, 64, "fp16", False, 71),
 ]
 
 
@@ -119,3 +122,17 @@ def test_workspace_contents_do_not_matter():
     b = eao.fwd_splitkv(tq, tk, tv, causal=True, num_splits=3)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_one_long_sequence_sampled_heads():
+    # one 131072-key sequence (automatic plan: 64 splits of 2048 keys per K/V head), a sample of
+    # heads against the oracle
+    B, Hq, Hkv, Nq, Nk, d = 1, 32, 8, 1, 131072, 128
+    q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=23)
+    o, lse = _run(q, k, v, True)
+    G = Hq // Hkv
+    for h in (0, 13, 31):
+        g = h // G
+        ro, rlse = DC.forward(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], True, 1.0 / np.sqrt(d))
+        assert np.abs(o[0, h] - ro[0, 0]).max() <= TOL_O["bf16"], h
+        assert np.abs(lse[0, h] - rlse[0, 0]).max() <= TOL_LSE, h
