@@ -21,6 +21,9 @@ Besides the headline value it carries:
     random N(0,1) operands (the kind of data the step multiplies) and on zero operands, each
     with its clock, and the step's rates as fractions of the random-operand rate (the matrix
     cores' power, and with it the clock, depends on the bits multiplied).
+The split-KV decoding legs (`--workload decode_bf16`, `decode4_bf16`) report K/V bytes per second
+instead, with `hbm_ceiling`: the HBM read rate this machine sustains in the decoding kernel's own
+load pattern with no compute, and the decoding rates as fractions of it.
 """
 from __future__ import annotations
 
@@ -280,6 +283,37 @@ def cpu_baseline_decode(w, q, k, v, target_s):
     }
 
 
+def hbm_ceiling(dev, rates):
+    """Attainable HBM read rate on this machine in the decoding kernel's pattern (attn_hbm_probe:
+    one-wave workgroups streaming 16 KB stages through a four-slot LDS ring with direct loads, no
+    compute) over a 1 GiB buffer, with 512 and 1024 workgroups, and each named rate as a
+    fraction of the better of the two.  The spec figure of 8 TB/s is not reached by reads."""
+    import torch
+
+    import exact_attention_online_amd as eao
+
+    gen = torch.Generator(device=dev).manual_seed(SEED)
+    data = torch.randint(-(1 << 31), (1 << 31) - 1, ((1 << 30) // 4,), dtype=torch.int32, device=dev, generator=gen)
+    res = {}
+    for groups in (512, 1024):
+        out = torch.empty(64 * groups, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            eao.hbm_probe(data, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nbytes = sum(eao.hbm_probe(data, out) for _ in range(10))
+        e1.record()
+        torch.cuda.synchronize()
+        res[groups] = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del data
+    best = max(res.values())
+    return {"stream_read_gbps": round(best, 1), "by_groups_gbps": {str(k): round(v, 1) for k, v in res.items()},
+            "frac_of_stream_read": {k: round(v / best, 4) for k, v in rates.items()},
+            "source": "attn_hbm_probe: 1 GiB read in 16 KB stages by 512 or 1024 one-wave workgroups, "
+                      "10 launches timed with events"}
+
+
 def bench_decode(args):
     """Split-KV decoding: K/V bytes streamed per second by attn_fwd_splitkv (split + merge kernels)."""
     import torch
@@ -369,6 +403,8 @@ def bench_decode(args):
     }
     out["graph_replay"] = {"ms_per_step": round(ms_graph, 5), "value": round(kv_bytes / (ms_graph * 1e-3) / 1e9, 1),
                            "unit": "GB/s"}
+    out["hbm_ceiling"] = hbm_ceiling(dev, {"two_kernels": out["roofline"]["achieved"], "call": value,
+                                           "graph_replay": out["graph_replay"]["value"]})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, qc, kc, vc, args.cpu_seconds)
     print(json.dumps(out), flush=True)

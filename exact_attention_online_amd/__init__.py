@@ -12,13 +12,13 @@ import os
 
 __all__ = [
     "load", "library_path", "fwd", "bwd", "bwd_phases", "fwd_fp8", "fp8_prep", "bwd_workspace_size",
-    "fwd_splitkv", "fwd_splitkv_noalloc", "splitkv_workspace_size", "attention", "clock_probe", "mfma_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
+    "fwd_splitkv", "fwd_splitkv_noalloc", "splitkv_workspace_size", "attention", "clock_probe", "mfma_probe", "hbm_probe", "fwd_ext", "bwd_ext", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_size", "AttnError", "EXPORTS", "F16", "BF16", "FP8_E4M3", "F32",
 ]
 
 F16, BF16, FP8_E4M3, F32 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd_ext", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_varlen", "attn_bwd_varlen_workspace_size", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_fp8_prep",
-           "attn_fwd_splitkv_noalloc", "attn_clock_probe", "attn_mfma_probe", "attn_status_string")
+           "attn_fwd_splitkv_noalloc", "attn_clock_probe", "attn_mfma_probe", "attn_hbm_probe", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -76,6 +76,8 @@ def load():
     lib.attn_clock_probe.restype = i
     lib.attn_mfma_probe.argtypes = [vp, ctypes.c_longlong, vp, i, i, vp]
     lib.attn_mfma_probe.restype = i
+    lib.attn_hbm_probe.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
+    lib.attn_hbm_probe.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -494,6 +496,24 @@ def mfma_probe(data, out, iters: int, stream=None):
     st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
     _check(load().attn_mfma_probe(_ptr(data), data.numel(), _ptr(out), groups, int(iters), ctypes.c_void_p(st)))
     return groups * 8 * 32 * int(iters) * 32768
+
+
+
+def hbm_probe(data, out, stream=None):
+    """Launch attn_hbm_probe: data is a contiguous device tensor (any dtype; its bytes a multiple
+    of 16384 * groups), out an int32 device tensor of 64 * groups entries that receives each
+    lane's sum modulo 2^32 of the 32-bit words it read; runs on `stream` (default: the current
+    stream).  Returns the number of bytes read."""
+    torch = _torch()
+    if not data.is_cuda or not data.is_contiguous():
+        raise AttnError("data must be a contiguous device tensor")
+    if out.dtype != torch.int32 or not out.is_cuda or not out.is_contiguous() or out.numel() % 64:
+        raise AttnError("out must be a contiguous int32 device tensor of 64 * groups entries")
+    groups = out.numel() // 64
+    nbytes = data.numel() * data.element_size()
+    st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
+    _check(load().attn_hbm_probe(_ptr(data), nbytes, _ptr(out), groups, ctypes.c_void_p(st)))
+    return nbytes
 
 
 _AttentionFn = None

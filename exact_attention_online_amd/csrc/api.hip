@@ -47,6 +47,7 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 hipError_t launch_clock_probe(unsigned long long* out, int groups, long long ticks, hipStream_t stream);
 hipError_t launch_mfma_probe(const uint16_t* data, size_t n, float* out, int groups, int iters, hipStream_t stream);
+hipError_t launch_hbm_probe(const uint8_t* data, uint32_t share, uint32_t* out, int groups, hipStream_t stream);
 size_t splitkv_scratch_bytes();
 hipError_t splitkv_scratch_address(void** out);
 }  // namespace eao
@@ -335,6 +336,15 @@ int attn_mfma_probe(const void* data, long long n, float* out, int groups, int i
   if (!aligned16(data) || !aligned16(out)) return ATTN_ERR_INVALID;
   if (n < 8192 || n % 8 != 0 || groups < 1 || groups > 65536 || iters < 1 || iters > (1 << 20)) return ATTN_ERR_INVALID;
   const hipError_t e = eao::launch_mfma_probe((const uint16_t*)data, (size_t)n, out, groups, iters, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_hbm_probe(const void* data, long long bytes, unsigned* out, int groups, attn_stream_t stream) {
+  if (!aligned16(data) || !aligned16(out)) return ATTN_ERR_INVALID;
+  if (groups < 1 || groups > 65536 || bytes <= 0 || bytes % ((long long)groups * 16384) != 0) return ATTN_ERR_INVALID;
+  const long long share = bytes / groups;
+  if (share > (1LL << 31)) return ATTN_ERR_INVALID;
+  const hipError_t e = eao::launch_hbm_probe((const uint8_t*)data, (uint32_t)share, out, groups, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

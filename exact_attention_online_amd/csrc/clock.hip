@@ -71,4 +71,79 @@ hipError_t launch_mfma_probe(const uint16_t* data, size_t n, float* out, int gro
   return hipGetLastError();
 }
 
+// HBM read probe, the third measurement aid: the rate at which the chip streams device memory into
+// LDS with the direct buffer -> LDS loads the kernels use, in the split-KV decoding kernel's
+// pattern.  Each workgroup is one wave that streams its contiguous share of `data` in 16 KB
+// stages through a ring of four LDS slots (distinct objects), requesting three stages ahead and
+// waiting on its vector-memory counter for the oldest stage only; each lane adds up, modulo 2^32,
+// the 32-bit words it brought in and stores the sum, so every byte is read and the result can be
+// checked.
+constexpr int kProbeStage = 16384;   // bytes per stage (16 direct loads of 1 KB)
+
+template <int n>
+__device__ __forceinline__ void probe_wait() {   // vmcnt n (bits 3:0 and 15:14), lgkmcnt 0
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
+}
+
+__global__ __launch_bounds__(64) void hbm_probe_kernel(const uint8_t* __restrict__ data, uint32_t share,
+                                                       uint32_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) short ring0[kProbeStage / 2];
+  __shared__ __attribute__((aligned(1024))) short ring1[kProbeStage / 2];
+  __shared__ __attribute__((aligned(1024))) short ring2[kProbeStage / 2];
+  __shared__ __attribute__((aligned(1024))) short ring3[kProbeStage / 2];
+  auto slot = [&](auto sl) __attribute__((always_inline)) -> short* {
+    constexpr int SL = decltype(sl)::value;
+    if constexpr (SL == 0) return ring0;
+    else if constexpr (SL == 1) return ring1;
+    else if constexpr (SL == 2) return ring2;
+    else return ring3;
+  };
+  const int lane = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(data + (size_t)blockIdx.x * share, share);
+  const int nst = (int)(share / kProbeStage);
+  auto issue = [&](int j, auto sl) __attribute__((always_inline)) {
+    short* dst = slot(sl);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) buffer_load16_lds(rs, dst + 512 * i, 16 * lane, (uint32_t)j * kProbeStage + 1024 * i);
+  };
+  uint32_t acc = 0;
+  auto stage = [&](int j, auto sl) __attribute__((always_inline)) {
+    constexpr int SL = decltype(sl)::value;
+    const int ahead = min(2, nst - 1 - j);
+    if (ahead >= 2) probe_wait<32>();
+    else if (ahead == 1) probe_wait<16>();
+    else probe_wait<0>();
+    if (j + 3 < nst) issue(j + 3, std::integral_constant<int, (SL + 3) % 4>{});
+    const short* src = slot(sl);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = *(const uint4*)(src + 512 * i + 8 * lane);
+      acc += v.x + v.y + v.z + v.w;
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if (nst > 0) issue(0, S0{});
+  if (nst > 1) issue(1, S1{});
+  if (nst > 2) issue(2, S2{});
+  for (int j = 0; j < nst; j += 4) {
+    stage(j, S0{});
+    if (j + 1 >= nst) break;
+    stage(j + 1, S1{});
+    if (j + 2 >= nst) break;
+    stage(j + 2, S2{});
+    if (j + 3 >= nst) break;
+    stage(j + 3, S3{});
+  }
+  out[(size_t)blockIdx.x * 64 + lane] = acc;
+}
+
+hipError_t launch_hbm_probe(const uint8_t* data, uint32_t share, uint32_t* out, int groups, hipStream_t stream) {
+  hipLaunchKernelGGL(hbm_probe_kernel, dim3(groups), dim3(64), 0, stream, data, share, out);
+  return hipGetLastError();
+}
+
 }  // namespace eao

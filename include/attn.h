@@ -272,6 +272,18 @@ int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_
  * attn_status_t. */
 int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, attn_stream_t stream);
 
+/* Measurement aid, not a step of the attention method: the rate at which the chip streams
+ * device memory into LDS with the direct buffer -> LDS loads of the kernels, in the split-KV
+ * decoding kernel's pattern, which bounds what a memory-bound kernel of that shape can reach.
+ * Launches `groups` workgroups of one wave; workgroup g streams bytes [g * share, (g + 1) * share)
+ * of `data` (device memory, read only; share = bytes / groups) in 16 KB stages through a ring of
+ * four LDS slots, requesting three stages ahead, and lane l of it writes to out[64 g + l] (groups
+ * * 64 unsigned words, device memory) the sum modulo 2^32 of the 32-bit words it loaded, so the
+ * sum of out modulo 2^32 is that of every 32-bit word of data.  data and out 16-byte aligned,
+ * 1 <= groups <= 65536, bytes > 0 a multiple of groups * 16384, share <= 2^31, else
+ * ATTN_ERR_INVALID.  Returns an attn_status_t. */
+int attn_hbm_probe(const void* data, long long bytes, unsigned* out, int groups, attn_stream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* attn_status_string(int status);
 

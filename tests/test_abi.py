@@ -236,6 +236,19 @@ def test_mfma_probe_rejects_bad_arguments():
     assert lib.attn_mfma_probe(P, 8192, P, 1, (1 << 20) + 1, NULL) == 1
 
 
+def test_hbm_probe_rejects_bad_arguments():
+    lib = eao.load()
+    assert lib.attn_hbm_probe(NULL, 16384, P, 1, NULL) == 1
+    assert lib.attn_hbm_probe(P, 16384, NULL, 1, NULL) == 1
+    assert lib.attn_hbm_probe(ctypes.c_void_p(0x7F0000001008), 16384, P, 1, NULL) == 1   # misaligned
+    assert lib.attn_hbm_probe(P, 0, P, 1, NULL) == 1
+    assert lib.attn_hbm_probe(P, 16384 * 3 + 1024, P, 3, NULL) == 1      # not whole 16 KB stages
+    assert lib.attn_hbm_probe(P, 16384 * 4, P, 3, NULL) == 1             # groups do not divide it
+    assert lib.attn_hbm_probe(P, 16384, P, 0, NULL) == 1
+    assert lib.attn_hbm_probe(P, 16384 * 65537, P, 65537, NULL) == 1
+    assert lib.attn_hbm_probe(P, (1 << 32), P, 1, NULL) == 1             # share past 2^31
+
+
 def test_splitkv_noalloc_rejects_on_the_host():
     """The allocation-free split-KV entry point checks its arguments, and that the problem's
     partials fit its static scratch, before any HIP call (so without a GPU too)."""

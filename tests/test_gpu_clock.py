@@ -1,6 +1,7 @@
 """The measurement aids beside the kernels.  Clock probe: every workgroup reports an engine clock
 within the part's range and real-time ticks covering the requested interval.  MFMA rate probe:
-its sums are exact on operands whose products are small integers."""
+its sums are exact on operands whose products are small integers.  HBM read probe: the sum of
+its outputs modulo 2^32 is that of every 32-bit word of the buffer (so every byte was read, once)."""
 import pytest
 import torch
 
@@ -33,3 +34,19 @@ def test_mfma_probe_sums_are_exact(value, iters):
     assert flops == 3 * 8 * 32 * iters * 32768
     want = 64 * 8 * iters * 16 * value * value
     assert torch.equal(out, torch.full_like(out, want))
+
+
+@pytest.mark.parametrize("stages, groups", [(1, 7), (2, 3), (3, 5), (5, 3), (16, 256)])
+def test_hbm_probe_reads_every_word_once(stages, groups):
+    dev = device()
+    g = torch.Generator(device=dev).manual_seed(stages * 100 + groups)
+    n = stages * groups * 16384 // 4
+    data = torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, device=dev, generator=g)
+    out = torch.full((64 * groups,), -1, dtype=torch.int32, device=dev)
+    assert eao.hbm_probe(data, out) == 4 * n
+    torch.cuda.synchronize()
+    mask = (1 << 32) - 1
+    assert (int(out.to(torch.int64).sum()) & mask) == (int(data.to(torch.int64).sum()) & mask)
+    # each lane's own words: lane l of group g sums bytes 16 l .. 16 l + 15 of every 1 KB piece
+    words = data.view(groups, -1, 64, 4).to(torch.int64).sum(dim=(1, 3)) & mask
+    assert torch.equal(out.view(groups, 64).to(torch.int64) & mask, words)
