@@ -23,7 +23,9 @@ Besides the headline value it carries:
     cores' power, and with it the clock, depends on the bits multiplied).
 The split-KV decoding legs (`--workload decode_bf16`, `decode4_bf16`) report K/V bytes per second
 instead, with `hbm_ceiling`: the HBM read rate this machine sustains in the decoding kernel's own
-load pattern with no compute, and the decoding rates as fractions of it.
+load pattern with no compute, and the decoding rates as fractions of it.  The fp8 leg
+(`--workload fp8`) carries its own `mfma_ceiling`: the fp8 MFMA rate on the workload's prepared
+codes and on zero codes.
 """
 from __future__ import annotations
 
@@ -680,7 +682,36 @@ def bench_fp8(args):
             "traffic": None,
         },
     }
+    out["mfma_ceiling"] = fp8_mfma_ceiling(dev, k8, {"fwd_fp8": out["roofline"]["achieved"]})
     print(json.dumps(out), flush=True)
+
+
+def fp8_mfma_ceiling(dev, codes, rates):
+    """Attainable dense fp8 MFMA rate on this machine (attn_mfma_probe in its e4m3 mode: back-to-back
+    v_mfma_scale_f32_32x32x64_f8f6f4, two waves per SIMD, no memory traffic) on the workload's own
+    prepared K codes and on zero codes, and each named rate as a fraction of the first."""
+    import torch
+
+    import exact_attention_online_amd as eao
+
+    res = {}
+    flat = codes.reshape(-1)
+    for name, data in (("workload_codes", flat[: (flat.numel() // 32) * 32]),
+                       ("zero", torch.zeros(1 << 20, dtype=torch.uint8, device=dev))):
+        out = torch.empty(512 * 1024, dtype=torch.float32, device=dev)
+        iters = 2000
+        eao.mfma_probe(data, out, iters)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(eao.mfma_probe(data, out, iters) for _ in range(3))
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"workload_codes_tflops": round(res["workload_codes"], 1), "zero_codes_tflops": round(res["zero"], 1),
+            "frac_of_workload_ceiling": {k: round(v / res["workload_codes"], 4) for k, v in rates.items()},
+            "source": "attn_mfma_probe (e4m3): 1024 workgroups x 8 waves x 32 x 2000 "
+                      "v_mfma_scale_f32_32x32x64_f8f6f4, 3 launches timed with events"}
 
 
 def bench_varlen(args, with_bwd=False):

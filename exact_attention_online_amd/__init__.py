@@ -74,7 +74,7 @@ def load():
     lib.attn_fp8_prep.restype = i
     lib.attn_clock_probe.argtypes = [vp, i, ctypes.c_longlong, vp]
     lib.attn_clock_probe.restype = i
-    lib.attn_mfma_probe.argtypes = [vp, ctypes.c_longlong, vp, i, i, vp]
+    lib.attn_mfma_probe.argtypes = [vp, ctypes.c_longlong, vp, i, i, i, vp]
     lib.attn_mfma_probe.restype = i
     lib.attn_hbm_probe.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
     lib.attn_hbm_probe.restype = i
@@ -484,19 +484,26 @@ def clock_probe(out, ticks: int, stream=None):
 
 
 def mfma_probe(data, out, iters: int, stream=None):
-    """Launch attn_mfma_probe: data is a contiguous bf16 device tensor (the operand bits, at
-    least 8192 values, a multiple of 8), out a float32 device tensor of 512 * groups entries;
-    runs on `stream` (default: the current stream).  Returns the launch's flop count."""
+    """Launch attn_mfma_probe: data is a contiguous device tensor of operand bits, bf16 values (at
+    least 8192, a multiple of 8) or uint8 e4m3 codes (at least 8192, a multiple of 32), out a
+    float32 device tensor of 512 * groups entries; runs on `stream` (default: the current
+    stream).  Returns the launch's flop count."""
     torch = _torch()
-    if data.dtype != torch.bfloat16 or not data.is_cuda or not data.is_contiguous():
-        raise AttnError("data must be a contiguous bf16 device tensor")
+    if data.dtype == torch.bfloat16:
+        dtype, per_mfma = BF16, 32768
+    elif data.dtype == torch.uint8:
+        dtype, per_mfma = FP8_E4M3, 131072
+    else:
+        raise AttnError("data must hold bf16 values or uint8 e4m3 codes")
+    if not data.is_cuda or not data.is_contiguous():
+        raise AttnError("data must be a contiguous device tensor")
     if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.numel() % 512:
         raise AttnError("out must be a contiguous float32 device tensor of 512 * groups entries")
     groups = out.numel() // 512
     st = (stream or torch.cuda.current_stream(out.device)).cuda_stream
-    _check(load().attn_mfma_probe(_ptr(data), data.numel(), _ptr(out), groups, int(iters), ctypes.c_void_p(st)))
-    return groups * 8 * 32 * int(iters) * 32768
-
+    _check(load().attn_mfma_probe(_ptr(data), data.numel(), _ptr(out), groups, int(iters), dtype,
+                                  ctypes.c_void_p(st)))
+    return groups * 8 * 32 * int(iters) * per_mfma
 
 
 def hbm_probe(data, out, stream=None):

@@ -46,7 +46,8 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               void* workspace, hipStream_t stream);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 hipError_t launch_clock_probe(unsigned long long* out, int groups, long long ticks, hipStream_t stream);
-hipError_t launch_mfma_probe(const uint16_t* data, size_t n, float* out, int groups, int iters, hipStream_t stream);
+hipError_t launch_mfma_probe(const void* data, size_t n, bool fp8, float* out, int groups, int iters,
+                             hipStream_t stream);
 hipError_t launch_hbm_probe(const uint8_t* data, uint32_t share, uint32_t* out, int groups, hipStream_t stream);
 size_t splitkv_scratch_bytes();
 hipError_t splitkv_scratch_address(void** out);
@@ -332,10 +333,15 @@ int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_
   return eao::launch_clock_probe(out, groups, ticks, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, attn_stream_t stream) {
+int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, int dtype,
+                    attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(data) || !aligned16(out)) return ATTN_ERR_INVALID;
-  if (n < 8192 || n % 8 != 0 || groups < 1 || groups > 65536 || iters < 1 || iters > (1 << 20)) return ATTN_ERR_INVALID;
-  const hipError_t e = eao::launch_mfma_probe((const uint16_t*)data, (size_t)n, out, groups, iters, (hipStream_t)stream);
+  const bool fp8 = dtype == ATTN_FP8_E4M3;
+  const long long unit = fp8 ? 32 : 8;          // values per operand fragment of one lane
+  if (n < 8192 || n % unit != 0 || groups < 1 || groups > 65536 || iters < 1 || iters > (1 << 20))
+    return ATTN_ERR_INVALID;
+  const hipError_t e = eao::launch_mfma_probe(data, (size_t)n, fp8, out, groups, iters, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

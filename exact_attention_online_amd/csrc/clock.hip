@@ -34,8 +34,8 @@ hipError_t launch_clock_probe(unsigned long long* out, int groups, long long tic
   return hipGetLastError();
 }
 
-// MFMA rate probe, the second measurement aid: the dense bf16 matrix-core rate the chip sustains
-// on given operand data.  The matrix cores' power depends on the bits they multiply, and under
+// MFMA rate probe, the second measurement aid: the dense bf16 (or fp8) matrix-core rate the chip
+// sustains on given operand data.  The matrix cores' power depends on the bits they multiply, and under
 // the board's power limit the engine clock follows, so random operands run well below the spec
 // peak while zero operands come close to it.  Each workgroup is 8 waves (two per SIMD of a compute
 // unit, as the attention kernels run); each wave loads 8 A and 8 B fragments (16 bytes per lane)
@@ -66,8 +66,45 @@ __global__ __launch_bounds__(512, 1) void mfma_probe_kernel(const uint16_t* __re
   out[(size_t)blockIdx.x * 512 + threadIdx.x] = x;
 }
 
-hipError_t launch_mfma_probe(const uint16_t* data, size_t n, float* out, int groups, int iters, hipStream_t stream) {
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3(groups), dim3(512), 0, stream, data, n, out, iters);
+// The same for fp8 e4m3 operands (`data` as bytes): 8 A and 8 B fragments of 32 bytes per lane and
+// iters x 32 back-to-back v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).
+typedef __attribute__((ext_vector_type(8))) int i32x8_probe_t;
+
+__global__ __launch_bounds__(512, 1) void mfma_probe_fp8_kernel(const uint8_t* __restrict__ data, size_t n,
+                                                                 float* __restrict__ out, int iters) {
+  i32x8_probe_t a[8], b[8];
+  auto frag = [&](size_t at) __attribute__((always_inline)) {
+    const uint4 lo = *(const uint4*)(data + at % n);
+    const uint4 hi = *(const uint4*)(data + (at + 16) % n);
+    return i32x8_probe_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = frag((size_t)blockIdx.x * 262144 + threadIdx.x * 512 + i * 32);
+    b[i] = frag((size_t)blockIdx.x * 262144 + threadIdx.x * 512 + 256 + i * 32);
+  }
+  f32x16_t acc[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + j) & 7], b[i], acc[j], 0, 0, 0, 127, 0, 127);
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x += acc[j][r];
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = x;
+}
+
+hipError_t launch_mfma_probe(const void* data, size_t n, bool fp8, float* out, int groups, int iters,
+                             hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL(mfma_probe_fp8_kernel, dim3(groups), dim3(512), 0, stream, (const uint8_t*)data, n, out, iters);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(groups), dim3(512), 0, stream, (const uint16_t*)data, n, out, iters);
   return hipGetLastError();
 }
 

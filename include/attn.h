@@ -258,19 +258,22 @@ int attn_fp8_prep(const float* x, uint8_t* x_fp8, float* descale, const int8_t* 
  * 1 <= ticks <= 10^9 (10 s), else ATTN_ERR_INVALID.  Returns an attn_status_t. */
 int attn_clock_probe(unsigned long long* out, int groups, long long ticks, attn_stream_t stream);
 
-/* Measurement aid, not a step of the attention method: the dense bf16 matrix-core rate on given
- * operand data.  The matrix cores draw power according to the bits they multiply and the engine
- * clock follows the board's power limit, so the attainable rate depends on the data: this
- * bounds what any bf16 kernel can reach on such inputs.  Launches `groups` workgroups of 512
- * threads (8 waves: two per SIMD of a compute unit); each wave loads 8 A and 8 B operand
- * fragments (16 bytes per lane) from `data` (n bfloat16 values, device memory, read only;
- * positions taken modulo n) and issues iters x 32 back-to-back v_mfma_f32_32x32x16_bf16 into four
- * fp32 accumulators; every thread then writes the sum of its accumulators to
- * out[512 * group + thread] (groups * 512 floats, device memory).  The launch does
- * groups * 8 * 32 * iters * 32768 flops.  data and out 16-byte aligned, n >= 8192 and a
- * multiple of 8, 1 <= groups <= 65536, 1 <= iters <= 2^20, else ATTN_ERR_INVALID.  Returns an
- * attn_status_t. */
-int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, attn_stream_t stream);
+/* Measurement aid, not a step of the attention method: the dense bf16 or fp8 matrix-core rate on
+ * given operand data.  The matrix cores draw power according to the bits they multiply and the
+ * engine clock follows the board's power limit, so the attainable rate depends on the data: this
+ * bounds what any kernel of that type can reach on such inputs.  Launches `groups` workgroups of
+ * 512 threads (8 waves: two per SIMD of a compute unit); each wave loads 8 A and 8 B operand
+ * fragments from `data` (n values, device memory, read only; positions taken modulo n) and
+ * issues iters x 32 back-to-back MFMAs into four fp32 accumulators: dtype ATTN_BF16, n bfloat16
+ * values, 16-byte fragments, v_mfma_f32_32x32x16_bf16 (32768 flops each); dtype ATTN_FP8_E4M3,
+ * n e4m3 codes, 32-byte fragments, v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (131072
+ * flops each).  Every thread then writes the sum of its accumulators to out[512 * group +
+ * thread] (groups * 512 floats, device memory).  The launch does groups * 8 * 32 * iters times
+ * the flops of one MFMA.  data and out 16-byte aligned, n >= 8192 and a multiple of 8 (bf16) or
+ * 32 (fp8), 1 <= groups <= 65536, 1 <= iters <= 2^20, else ATTN_ERR_INVALID; another dtype,
+ * ATTN_ERR_UNSUPPORTED.  Returns an attn_status_t. */
+int attn_mfma_probe(const void* data, long long n, float* out, int groups, int iters, int dtype,
+                    attn_stream_t stream);
 
 /* Measurement aid, not a step of the attention method: the rate at which the chip streams
  * device memory into LDS with the direct buffer -> LDS loads of the kernels, in the split-KV

@@ -225,15 +225,18 @@ def test_clock_probe_rejects_bad_arguments():
 
 def test_mfma_probe_rejects_bad_arguments():
     lib = eao.load()
-    assert lib.attn_mfma_probe(NULL, 8192, P, 1, 1, NULL) == 1
-    assert lib.attn_mfma_probe(P, 8192, NULL, 1, 1, NULL) == 1
-    assert lib.attn_mfma_probe(ctypes.c_void_p(0x7F0000001008), 8192, P, 1, 1, NULL) == 1   # misaligned
-    assert lib.attn_mfma_probe(P, 8184, P, 1, 1, NULL) == 1          # fewer than 8192 values
-    assert lib.attn_mfma_probe(P, 8196, P, 1, 1, NULL) == 1          # not a multiple of 8
-    assert lib.attn_mfma_probe(P, 8192, P, 0, 1, NULL) == 1
-    assert lib.attn_mfma_probe(P, 8192, P, 65537, 1, NULL) == 1
-    assert lib.attn_mfma_probe(P, 8192, P, 1, 0, NULL) == 1
-    assert lib.attn_mfma_probe(P, 8192, P, 1, (1 << 20) + 1, NULL) == 1
+    BF, F8 = 1, 2
+    assert lib.attn_mfma_probe(NULL, 8192, P, 1, 1, BF, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, NULL, 1, 1, BF, NULL) == 1
+    assert lib.attn_mfma_probe(ctypes.c_void_p(0x7F0000001008), 8192, P, 1, 1, BF, NULL) == 1   # misaligned
+    assert lib.attn_mfma_probe(P, 8184, P, 1, 1, BF, NULL) == 1          # fewer than 8192 values
+    assert lib.attn_mfma_probe(P, 8196, P, 1, 1, BF, NULL) == 1          # not a multiple of 8
+    assert lib.attn_mfma_probe(P, 8192 + 16, P, 1, 1, F8, NULL) == 1     # fp8: not a multiple of 32
+    assert lib.attn_mfma_probe(P, 8192, P, 0, 1, BF, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 65537, 1, BF, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 1, 0, F8, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 1, (1 << 20) + 1, BF, NULL) == 1
+    assert lib.attn_mfma_probe(P, 8192, P, 1, 1, 0, NULL) == 2           # fp16: not offered
 
 
 def test_hbm_probe_rejects_bad_arguments():

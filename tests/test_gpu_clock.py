@@ -1,6 +1,6 @@
 """The measurement aids beside the kernels.  Clock probe: every workgroup reports an engine clock
 within the part's range and real-time ticks covering the requested interval.  MFMA rate probe:
-its sums are exact on operands whose products are small integers.  HBM read probe: the sum of
+its sums are exact on operands whose products are small integers, bf16 and fp8.  HBM read probe: the sum of
 its outputs modulo 2^32 is that of every 32-bit word of the buffer (so every byte was read, once)."""
 import pytest
 import torch
@@ -33,6 +33,20 @@ def test_mfma_probe_sums_are_exact(value, iters):
     torch.cuda.synchronize()
     assert flops == 3 * 8 * 32 * iters * 32768
     want = 64 * 8 * iters * 16 * value * value
+    assert torch.equal(out, torch.full_like(out, want))
+
+
+@pytest.mark.parametrize("code, value, iters", [(0x38, 1.0, 2), (0x00, 0.0, 1), (0x40, 2.0, 3), (0xB8, -1.0, 1)])
+def test_mfma_probe_fp8_sums_are_exact(code, value, iters):
+    """fp8 e4m3 operands all equal to x (0x38 = 1, 0x40 = 2, 0xB8 = -1): each MFMA adds 64 x^2 to
+    every accumulator element, 8 MFMAs per accumulator and iteration, 4 x 16 elements a thread."""
+    dev = device()
+    data = torch.full((1 << 16,), code, dtype=torch.uint8, device=dev)
+    out = torch.full((512 * 2,), -1.0, dtype=torch.float32, device=dev)
+    flops = eao.mfma_probe(data, out, iters)
+    torch.cuda.synchronize()
+    assert flops == 2 * 8 * 32 * iters * 131072
+    want = 64 * 8 * iters * 64 * value * value
     assert torch.equal(out, torch.full_like(out, want))
 
 
