@@ -248,12 +248,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) float st2[512];
   // P of each key quarter: [quarter][slot 2 * half + t][lane], 16 bytes each
   __shared__ __attribute__((aligned(1024))) uint4 pex[4 * 4 * 64];
-  auto QD = [&](auto par) -> short* __attribute__((always_inline)) {
+  auto QD = [&](auto par) __attribute__((always_inline)) -> short* {
     if constexpr (decltype(par)::value == 0) return qd0;
     else if constexpr (decltype(par)::value == 1) return qd1;
     else return qd2;
   };
-  auto ST = [&](auto par) -> float* __attribute__((always_inline)) {
+  auto ST = [&](auto par) __attribute__((always_inline)) -> float* {
     if constexpr (decltype(par)::value == 0) return st0;
     else if constexpr (decltype(par)::value == 1) return st1;
     else return st2;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     s0 = sr.s0;
   }
   // first row of a head (of this sequence) in the [B,H,N,d] or packed [H,T,d] tensors
-  auto head_row0 = [&](int bh_b, int hh) -> size_t __attribute__((always_inline)) {
+  auto head_row0 = [&](int bh_b, int hh) __attribute__((always_inline)) -> size_t {
     if constexpr (VARLEN) return (size_t)hh * N_in + s0;
     else return (size_t)bh_b * N;
   };
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(ROWS * 2, 512 / (ROWS * 2)) void bwd_dq_kernel(
   constexpr int PW = PIECES / NW;                   // pieces per wave per tile
   __shared__ __attribute__((aligned(1024))) short kv0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) short kv1[2 * TILE];
-  auto KV = [&](auto par) -> short* __attribute__((always_inline)) {
+  auto KV = [&](auto par) __attribute__((always_inline)) -> short* {
     if constexpr (decltype(par)::value == 0) return kv0; else return kv1;
   };
 

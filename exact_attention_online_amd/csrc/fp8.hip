@@ -244,10 +244,10 @@ __global__ __launch_bounds__(NWV * 64, NWV == 8 ? 1 : 2) void fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE];
-  auto Ks = [&](auto par) -> uint8_t* __attribute__((always_inline)) {
+  auto Ks = [&](auto par) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
   };
-  auto Vs = [&](auto par) -> uint8_t* __attribute__((always_inline)) {
+  auto Vs = [&](auto par) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
   };
 
