@@ -36,6 +36,13 @@ def test_host_tensors_are_rejected_before_any_call(monkeypatch):
         eao.fwd_varlen(q[0], q[0], q[0], torch.tensor([0, 8], dtype=torch.int32), 8)
     with pytest.raises(eao.AttnError):
         eao.fp8_prep(torch.zeros(1, 2, 8, 128))
+    # the measurement aids: host tensors, and operand types the MFMA probe does not take
+    with pytest.raises(eao.AttnError, match="device"):
+        eao.mfma_probe(torch.zeros(8192, dtype=torch.bfloat16), torch.zeros(512), 1)
+    with pytest.raises(eao.AttnError, match="bf16 values or uint8"):
+        eao.mfma_probe(torch.zeros(8192, dtype=torch.float16), torch.zeros(512), 1)
+    with pytest.raises(eao.AttnError, match="device"):
+        eao.hbm_probe(torch.zeros(4096, dtype=torch.int32), torch.zeros(64, dtype=torch.int32))
 
 
 def _bench(*args, env=None):
