@@ -304,12 +304,20 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  // the first 64 logsumexps are loaded once, for the maximum and for the weights
+  // the first 64 logsumexps are loaded once, for the maximum and for the weights; the first 16
+  // splits' partial outputs are requested at the same time (they do not depend on the weights)
   const float ls0 = lane < S ? Lpart[(size_t)lane * rows + row] : -INFINITY;
+  const bool act = lane < D / 2;
+  const size_t step = (size_t)rows * D;             // floats from one split's row to the next's
+  const int n0 = min(64, S);
+  float2 ov0[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    ov0[u] = act ? *(const float2*)(Opart + (size_t)row * D + 2 * lane + (size_t)min(u, n0 - 1) * step)
+                 : float2{0.f, 0.f};
   float mx = ls0;
   for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
   mx = wave_max(mx);
-  const bool act = lane < D / 2;
   float a0 = 0.f, a1 = 0.f, wpart = 0.f;
   auto weight = [](float w, int i) __attribute__((always_inline)) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
@@ -320,14 +328,18 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
     wpart += wgt;
     const int n = min(64, S - c);
     const float* op = Opart + ((size_t)c * rows + row) * D + 2 * lane;
-    const size_t step = (size_t)rows * D;           // floats from one split's row to the next's
     // batches of 16 splits with their loads in flight together; past the chunk's last split the
     // index stays on that split and the weight (held by a lane past S) is zero
     for (int i = 0; i < n; i += 16) {
       float2 ov[16];
+      if (c == 0 && i == 0) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        ov[u] = act ? *(const float2*)(op + (size_t)min(i + u, n - 1) * step) : float2{0.f, 0.f};
+        for (int u = 0; u < 16; ++u) ov[u] = ov0[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          ov[u] = act ? *(const float2*)(op + (size_t)min(i + u, n - 1) * step) : float2{0.f, 0.f};
+      }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const float w = weight(wgt, i + u);
